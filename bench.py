@@ -1,0 +1,242 @@
+"""Throughput of the weighted MQA-logits hot path on one MI355X.
+
+Default workload: dense clean logits, Sq=2048 query rows, Skv=32768 keys,
+H=64 heads, D=128, fp8 e4m3 Q/KV with fp32 per-token scales and weights, row i
+covering keys [0, Skv - Sq + i) -- the indexer prefill shape.  One step = one
+full call of the path on inputs already resident in HBM.  Metric: effective
+TFLOP/s = 2 * H * D * (in-range entries) / time; masked and -inf entries are
+not counted.
+
+Prints one JSON line.  Other workloads (--workload) are for measurement notes.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MQA-logits effective TFLOP/s + % fp8 MFMA peak (H64 D128, 2K×32K)"
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4-mxfp8": 4, "c4-mxfp4": 4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def clamped_ranges(k_start, k_end, skv):
+    """Row ranges as the metric counts them: [clamp(s,0,Skv), clamp(e,s,Skv))."""
+    s = np.clip(np.asarray(k_start, np.int64), 0, skv)
+    return s, np.clip(np.asarray(k_end, np.int64), s, skv)
+
+
+def valid_entries_dense(case):
+    s, e = clamped_ranges(case.k_start, case.k_end, case.skv)
+    return int((e - s).sum())
+
+
+def check_mask(out, case, rows_per_chunk=128):
+    """-inf exactly outside each row's range, finite inside (checked before timing)."""
+    import torch
+    s, e = clamped_ranges(case.k_start, case.k_end, case.skv)
+    S, E = torch.from_numpy(s).cuda(), torch.from_numpy(e).cuda()
+    cols = torch.arange(case.skv, device="cuda")
+    for r0 in range(0, case.sq, rows_per_chunk):
+        r1 = min(r0 + rows_per_chunk, case.sq)
+        valid = (cols[None, :] >= S[r0:r1, None]) & (cols[None, :] < E[r0:r1, None])
+        chunk = out[r0:r1]
+        if not (torch.equal(torch.isneginf(chunk), ~valid) and bool(torch.isfinite(chunk[valid]).all())):
+            raise SystemExit(f"mask check failed in rows [{r0}, {r1})")
+
+
+def build_step(name):
+    """Returns (step_fn, info dict) with inputs resident on cuda:0."""
+    import torch
+    import mqa_logits_amd as mq
+    import synth
+
+    idx = WORKLOADS[name]
+    fmt = name.split("-")[1] if name.startswith("c4") else None
+    case = synth.config_case(idx, fmt)
+    dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    info = dict(workload=synth.CONFIG_NAMES[idx] + (f"_{fmt}" if fmt else ""), case=case)
+
+    if idx in (0, 1, 4):
+        d = [dev(x) for x in case.args()[1:]]
+        q, q_sf, kv, kv_sf, kvs, w, ks, ke = d
+        n_out = 2 if idx == 4 else 4          # distinct output buffers, rotated
+        outs = [torch.empty(case.sq, case.skv, dtype=torch.float32, device="cuda")
+                for _ in range(n_out)]
+        state = {"i": 0}
+
+        def step():
+            o = outs[state["i"] % n_out]
+            state["i"] += 1
+            mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o)
+        nvalid = valid_entries_dense(case)
+        info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
+                    sq=case.sq, skv=case.skv, h=case.h, d=case.d, outs=outs,
+                    cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
+                             format=case.fmt, layout="dense", clean_logits=True))
+        # mask check before timing (the pages' reproducer checks the mask too)
+        step()
+        torch.cuda.synchronize()
+        check_mask(outs[0], case)
+        return step, info
+
+    if idx == 2:
+        d = [dev(x) for x in case.args()[1:]]
+        q, q_sf, kv, kv_sf, kvs, w, ks, ke = d
+        off = mq.mqa_logits_compressed_offsets(ks, ke, case.skv)
+        total = int(off[-1].item())
+        outs = [torch.empty(total, dtype=torch.float32, device="cuda") for _ in range(4)]
+        state = {"i": 0}
+
+        def step():
+            o = outs[state["i"] % 4]
+            state["i"] += 1
+            mq.mqa_logits_compressed_offsets(ks, ke, case.skv, out=off)
+            mq.mqa_logits_compressed(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke,
+                                     row_offsets=off, out=o)
+        nvalid = valid_entries_dense(case)
+        info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
+                    cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
+                             format=case.fmt, layout="compressed"))
+        return step, info
+
+    # paged decode
+    pd = dict(q=dev(case.q), q_sf=dev(case.q_sf), kv=dev(case.kv_pool),
+              kv_sf=dev(case.kv_sf_pool), kvs=dev(case.kv_scale_pool), w=dev(case.weights),
+              ctx=dev(case.context_lens), bt=dev(case.block_table))
+    splits = mq.paged_mqa_logits_default_splits(0)
+    sched = mq.paged_mqa_logits_metadata(pd["ctx"], case.next_n, case.block_size,
+                                         case.max_context_len, splits)
+    rows = case.batch * case.next_n
+    outs = [torch.empty(rows, case.max_context_len, dtype=torch.float32, device="cuda")
+            for _ in range(4)]
+    state = {"i": 0}
+
+    def step():
+        o = outs[state["i"] % 4]
+        state["i"] += 1
+        mq.paged_mqa_logits_metadata(pd["ctx"], case.next_n, case.block_size,
+                                     case.max_context_len, splits, out=sched)
+        mq.paged_mqa_logits(case.fmt, pd["q"], pd["q_sf"], pd["kv"], pd["kv_sf"], pd["kvs"],
+                            pd["w"], pd["ctx"], pd["bt"], sched, case.next_n,
+                            case.max_context_len, out=o)
+    ctx = np.asarray(case.context_lens, np.int64)
+    length = np.minimum(ctx, case.max_context_len)
+    t = np.arange(case.next_n)
+    nvalid = int(np.clip(ctx[:, None] - case.next_n + t[None, :] + 1, 0, length[:, None]).sum())
+    n_units = int(((length + case.block_size - 1) // case.block_size).sum())
+    row_bytes = case.d * (1 if case.fmt != "mxfp4" else 0.5)
+    kv_bytes = n_units * case.block_size * (row_bytes + 4)
+    out_bytes = rows * case.max_context_len * 4
+    info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="hbm",
+                bytes=kv_bytes + out_bytes + case.q.nbytes + case.weights.nbytes,
+                cfg=dict(batch=case.batch, next_n=case.next_n, heads=case.h, head_dim=case.d,
+                         block_size=case.block_size, max_context_len=case.max_context_len,
+                         format=case.fmt, layout="paged", splits=splits))
+    return step, info
+
+
+def cpu_baseline(info, seconds):
+    """The oracle, as it stands, on leading rows of the same workload."""
+    import oracle                          # the oracle is used by this leg only
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    case = info["case"]
+    if not hasattr(case, "sq"):
+        return None
+    s, e = clamped_ranges(case.k_start, case.k_end, case.skv)
+    t0 = time.perf_counter()
+    done, flops, block = 0, 0.0, 8
+    while done < case.sq and time.perf_counter() - t0 < seconds:
+        rows = np.arange(done, min(done + block, case.sq))
+        oracle.dense_logits(*case.args(), rows=rows, row_block=block)
+        flops += 2.0 * case.h * case.d * float((e[rows] - s[rows]).sum())
+        done = rows[-1] + 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{done - 1} of the same workload (float64 numpy oracle), "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards without communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    step, info = build_step(args.workload)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-launch HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    flops = info["flops"]
+    value = flops * args.steps / wall / 1e12
+    if info["bound"] == "mfma":
+        achieved = flops / (per_launch_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[info["fmt"]]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
+    else:
+        achieved = info["bytes"] / (per_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(info, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp8": "fp8_e4m3", "mxfp8": "mxfp8_e4m3", "mxfp4": "mxfp4_e2m1"}[info["fmt"]],
+        "data": "synthetic",
+        "config": {"workload": info["workload"], **info["cfg"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_ms": per_launch_ms,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

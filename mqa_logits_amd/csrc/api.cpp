@@ -1,0 +1,285 @@
+// C ABI of the weighted MQA-logits library: argument validation on the host
+// (before any HIP call), kernel-configuration choice and launch on the
+// caller's stream.  Declarations and contracts live in include/mqa_logits.h.
+#include "mqa_logits.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mqa_status fail(mqa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mqa_status ok() {
+  g_last_error.clear();
+  return MQA_OK;
+}
+
+mqa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MQA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The kernels address each wave's output rows and the KV array through raw
+// buffer resources with 32-bit offsets; every such range must stay below this
+// many bytes (the kernels' out-of-range marker sits just above it).
+constexpr int64_t kMaxRangeBytes = 0x7ff00000;
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("MQA_LOGITS_DEBUG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+// Shared checks of the element formats and head shape.
+mqa_status check_common(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
+                        const uint8_t* kv_sf, const float* kv_scale, const float* weights,
+                        int32_t h, int32_t d, const char* who) {
+  if (dt != MQA_FP8_E4M3 && dt != MQA_MXFP8_E4M3 && dt != MQA_MXFP4_E2M1)
+    return fail(MQA_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dt);
+  if (h != 8 && h != 16 && h != 32 && h != 64)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: H=%d not supported (8, 16, 32, 64)", who, h);
+  if (d != 64 && d != 128)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: D=%d not supported (64, 128)", who, d);
+  if (!q || !kv || !weights) return fail(MQA_ERR_INVALID_ARG, "%s: null q, kv or weights", who);
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(weights, 16))
+    return fail(MQA_ERR_INVALID_ARG, "%s: q, kv and weights must be 16-byte aligned", who);
+  if (dt == MQA_FP8_E4M3) {
+    if (q_sf || kv_sf) return fail(MQA_ERR_INVALID_ARG, "%s: FP8 takes no block scales", who);
+    if (!kv_scale) return fail(MQA_ERR_INVALID_ARG, "%s: FP8 needs kv_scale", who);
+    if (!aligned(kv_scale, 4)) return fail(MQA_ERR_INVALID_ARG, "%s: kv_scale misaligned", who);
+  } else {
+    if (!q_sf || !kv_sf) return fail(MQA_ERR_INVALID_ARG, "%s: MX formats need q_sf and kv_sf", who);
+    if (kv_scale) return fail(MQA_ERR_INVALID_ARG, "%s: MX formats take no kv_scale", who);
+  }
+  return MQA_OK;
+}
+
+// Columns per block: enough blocks to give every compute unit several, with
+// chunks of at least 256 tokens.  Any multiple of 16 is correct.
+int32_t pick_chunk(int32_t sq, int32_t skv) {
+  const int64_t qblocks = (sq + 3) / 4;          // one wave (block) per 4 rows
+  const int64_t target_blocks = 8192;
+  int64_t n_chunks = (target_blocks + qblocks - 1) / qblocks;
+  const int64_t max_chunks = (skv + 255) / 256;
+  if (n_chunks > max_chunks) n_chunks = max_chunks;
+  if (n_chunks < 1) n_chunks = 1;
+  int64_t cols = (skv + n_chunks - 1) / n_chunks;
+  cols = (cols + 15) & ~int64_t(15);
+  if (cols < 16) cols = 16;
+  return (int32_t)cols;
+}
+
+mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
+                     const uint8_t* kv_sf, const float* kv_scale, const float* weights,
+                     const int32_t* k_start, const int32_t* k_end, const int64_t* row_off,
+                     float* out, int64_t stride, int32_t sq, int32_t skv, int32_t h, int32_t d,
+                     int store, hipStream_t stream, const char* who) {
+  const int64_t row_bytes = (dt == MQA_MXFP4_E2M1 ? d / 2 : d);
+  if ((int64_t)skv * row_bytes >= kMaxRangeBytes || (int64_t)skv * 16 >= kMaxRangeBytes)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: Skv=%d too large", who, skv);
+  mqa::DenseParams p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.q_sf = q_sf;
+  p.kv = static_cast<const uint8_t*>(kv);
+  p.kv_sf = kv_sf;
+  p.kv_scale = kv_scale;
+  p.w = weights;
+  p.k_start = k_start;
+  p.k_end = k_end;
+  p.row_off = row_off;
+  p.out = out;
+  p.stride = stride;
+  p.sq = sq;
+  p.skv = skv;
+  p.chunk_cols = pick_chunk(sq, skv);
+  p.n_chunks = (skv + p.chunk_cols - 1) / p.chunk_cols;
+  const int64_t grid = (int64_t)((sq + 3) / 4) * p.n_chunks;
+  if (grid > 0x7fffffff) return fail(MQA_ERR_UNSUPPORTED, "%s: problem too large", who);
+  if (debug_enabled())
+    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d store=%d Sq=%d Skv=%d chunk=%d grid=%lld\n",
+            who, (int)dt, h, d, store, sq, skv, p.chunk_cols, (long long)grid);
+  return hip_status(mqa::launch_dense((int)dt, h, d, store, p, stream), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mqa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mqa_num_cus(int32_t device) {
+  int n = 0;
+  hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) {
+    fail(MQA_ERR_HIP, "mqa_num_cus: %s", hipGetErrorString(e));
+    return -1;
+  }
+  return n;
+}
+
+int32_t paged_mqa_logits_default_splits(int32_t device) {
+  const int32_t n = mqa_num_cus(device);
+  return n < 0 ? n : n * mqa::kWavesPerCu;
+}
+
+mqa_status mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
+                      const uint8_t* kv_sf, const float* kv_scale, const float* weights,
+                      const int32_t* k_start, const int32_t* k_end, float* logits,
+                      int64_t logits_stride, int32_t sq, int32_t skv, int32_t h, int32_t d,
+                      int32_t clean_logits, hipStream_t stream) {
+  const char* who = "mqa_logits";
+  if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
+  if (logits_stride < skv) return fail(MQA_ERR_INVALID_ARG, "%s: logits_stride < Skv", who);
+  if (sq == 0 || skv == 0) return ok();
+  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, h, d, who);
+  if (st != MQA_OK) return st;
+  if (!k_start || !k_end || !logits) return fail(MQA_ERR_INVALID_ARG, "%s: null ranges or logits", who);
+  if (!aligned(k_start, 4) || !aligned(k_end, 4) || !aligned(logits, 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: ranges or logits misaligned", who);
+  if (logits_stride * 4 * 4 >= kMaxRangeBytes)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: logits_stride %lld too large", who, (long long)logits_stride);
+  return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, nullptr, logits,
+                   logits_stride, sq, skv, h, d, clean_logits ? mqa::kDenseClean : mqa::kDenseKeep,
+                   stream, who);
+}
+
+mqa_status mqa_logits_compressed_offsets(const int32_t* k_start, const int32_t* k_end, int32_t sq,
+                                         int32_t skv, int64_t* row_offsets, hipStream_t stream) {
+  const char* who = "mqa_logits_compressed_offsets";
+  if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
+  if (!row_offsets || (sq > 0 && (!k_start || !k_end)))
+    return fail(MQA_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned(row_offsets, 8) || !aligned(k_start, 4) || !aligned(k_end, 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  return hip_status(mqa::launch_compressed_offsets(k_start, k_end, sq, skv, row_offsets, stream), who);
+}
+
+mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
+                                 const uint8_t* kv_sf, const float* kv_scale, const float* weights,
+                                 const int32_t* k_start, const int32_t* k_end,
+                                 const int64_t* row_offsets, float* logits_packed, int32_t sq,
+                                 int32_t skv, int32_t h, int32_t d, hipStream_t stream) {
+  const char* who = "mqa_logits_compressed";
+  if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
+  if (sq == 0 || skv == 0) return ok();
+  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, h, d, who);
+  if (st != MQA_OK) return st;
+  if (!k_start || !k_end || !row_offsets || !logits_packed)
+    return fail(MQA_ERR_INVALID_ARG, "%s: null ranges, offsets or output", who);
+  if (!aligned(k_start, 4) || !aligned(k_end, 4) || !aligned(row_offsets, 8) ||
+      !aligned(logits_packed, 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, row_offsets,
+                   logits_packed, 0, sq, skv, h, d, mqa::kCompressed, stream, who);
+}
+
+int64_t paged_mqa_logits_metadata_size(int32_t num_splits) {
+  return num_splits < 1 ? -1 : 2 * (int64_t)(num_splits + 1);
+}
+
+static mqa_status check_paged_shape(int32_t batch, int32_t next_n, int32_t block_size,
+                                    int32_t max_context_len, int32_t num_splits, const char* who) {
+  if (batch < 1 || batch > 8192) return fail(MQA_ERR_UNSUPPORTED, "%s: batch=%d not in [1, 8192]", who, batch);
+  if (next_n < 1 || next_n > 4) return fail(MQA_ERR_UNSUPPORTED, "%s: next_n=%d not in [1, 4]", who, next_n);
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: block_size=%d not in {16, 32, 64}", who, block_size);
+  if (max_context_len < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative max_context_len", who);
+  if (num_splits < 1 || num_splits > 65536)
+    return fail(MQA_ERR_INVALID_ARG, "%s: num_splits=%d not in [1, 65536]", who, num_splits);
+  const int64_t nb_max = ((int64_t)max_context_len + block_size - 1) / block_size;
+  if ((int64_t)batch * nb_max >= 0x7fffffff)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: batch * blocks per sequence overflows int32", who);
+  return MQA_OK;
+}
+
+mqa_status paged_mqa_logits_metadata(const int32_t* context_lens, int32_t batch, int32_t next_n,
+                                     int32_t block_size, int32_t max_context_len, int32_t num_splits,
+                                     int32_t* schedule, hipStream_t stream) {
+  const char* who = "paged_mqa_logits_metadata";
+  mqa_status st = check_paged_shape(batch, next_n, block_size, max_context_len, num_splits, who);
+  if (st != MQA_OK) return st;
+  if (!context_lens || !schedule) return fail(MQA_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned(context_lens, 4) || !aligned(schedule, 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  return hip_status(mqa::launch_paged_metadata(context_lens, batch, block_size, max_context_len,
+                                               num_splits, schedule, stream),
+                    who);
+}
+
+mqa_status paged_mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv_pool,
+                            const uint8_t* kv_sf_pool, const float* kv_scale_pool,
+                            const float* weights, const int32_t* context_lens,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            const int32_t* schedule, float* logits, int64_t logits_stride,
+                            int32_t batch, int32_t next_n, int32_t h, int32_t d,
+                            int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                            int32_t num_splits, int32_t clean_logits, hipStream_t stream) {
+  const char* who = "paged_mqa_logits";
+  mqa_status st = check_paged_shape(batch, next_n, block_size, max_context_len, num_splits, who);
+  if (st != MQA_OK) return st;
+  st = check_common(dt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights, h, d, who);
+  if (st != MQA_OK) return st;
+  if (num_blocks < 1) return fail(MQA_ERR_INVALID_ARG, "%s: num_blocks < 1", who);
+  if (!context_lens || !block_table || !schedule || !logits)
+    return fail(MQA_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (logits_stride < max_context_len)
+    return fail(MQA_ERR_INVALID_ARG, "%s: logits_stride < max_context_len", who);
+  const int64_t nb_max = ((int64_t)max_context_len + block_size - 1) / block_size;
+  if (block_table_stride < nb_max)
+    return fail(MQA_ERR_INVALID_ARG, "%s: block_table_stride < ceil(max_context_len / block_size)", who);
+  if (!aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(schedule, 4) ||
+      !aligned(logits, 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  if ((int64_t)next_n * logits_stride * 4 >= kMaxRangeBytes)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: logits_stride %lld too large", who, (long long)logits_stride);
+  if ((int64_t)num_blocks * block_size * 4 >= kMaxRangeBytes)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: pool of %d blocks too large", who, num_blocks);
+  if (max_context_len == 0) return ok();
+  mqa::PagedParams p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.q_sf = q_sf;
+  p.kv = static_cast<const uint8_t*>(kv_pool);
+  p.kv_sf = kv_sf_pool;
+  p.kv_scale = kv_scale_pool;
+  p.w = weights;
+  p.ctx = context_lens;
+  p.bt = block_table;
+  p.bt_stride = block_table_stride;
+  p.sched = schedule;
+  p.out = logits;
+  p.stride = logits_stride;
+  p.batch = batch;
+  p.next_n = next_n;
+  p.bs = block_size;
+  p.num_blocks = num_blocks;
+  p.max_ctx = max_context_len;
+  p.num_splits = num_splits;
+  p.nb_max = (int32_t)nb_max;
+  if (debug_enabled())
+    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d batch=%d next_n=%d bs=%d splits=%d\n", who,
+            (int)dt, h, d, batch, next_n, block_size, num_splits);
+  return hip_status(mqa::launch_paged((int)dt, h, d, clean_logits ? 1 : 0, p, stream), who);
+}
+
+}  // extern "C"

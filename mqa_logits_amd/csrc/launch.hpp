@@ -1,0 +1,59 @@
+// Kernel parameter blocks and host-side launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+// Output modes of the dense kernel.
+enum Store : int { kDenseClean = 0, kDenseKeep = 1, kCompressed = 2 };
+
+// Waves per block of the dense and paged kernels.  One: every value a wave
+// needs to be uniform (its rows, its chunk, its buffer resources) then comes
+// from blockIdx and the kernel arguments, which live in SGPRs already.
+constexpr int kWavesPerBlock = 1;
+// Resident waves per compute unit the kernels are sized for (one per SIMD).
+constexpr int kWavesPerCu = 4;
+
+struct DenseParams {
+  const uint8_t* q;        // [Sq, H, D] bytes (fp4: D/2)
+  const uint8_t* q_sf;     // [Sq, H, D/32] or null
+  const uint8_t* kv;       // [Skv, D] bytes (fp4: D/2)
+  const uint8_t* kv_sf;    // [Skv, D/32] or null
+  const float* kv_scale;   // [Skv] (FP8) or null
+  const float* w;          // [Sq, H]
+  const int32_t* k_start;  // [Sq]
+  const int32_t* k_end;    // [Sq]
+  const int64_t* row_off;  // [Sq + 1] (compressed) or null
+  float* out;
+  int64_t stride;          // dense row stride in elements
+  int32_t sq, skv;
+  int32_t chunk_cols;      // KV columns per block, a multiple of 16
+  int32_t n_chunks;        // ceil(Skv / chunk_cols)
+};
+
+struct PagedParams {
+  const uint8_t* q;          // [batch*next_n, H, D]
+  const uint8_t* q_sf;
+  const uint8_t* kv;         // [num_blocks, bs, D]
+  const uint8_t* kv_sf;      // [num_blocks, bs, D/32]
+  const float* kv_scale;     // [num_blocks, bs]
+  const float* w;            // [batch*next_n, H]
+  const int32_t* ctx;        // [batch]
+  const int32_t* bt;         // [batch, bt_stride]
+  int64_t bt_stride;
+  const int32_t* sched;      // [num_splits + 1][2]
+  float* out;
+  int64_t stride;
+  int32_t batch, next_n, bs, num_blocks, max_ctx, num_splits, nb_max;
+};
+
+hipError_t launch_dense(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
+hipError_t launch_compressed_offsets(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
+                                     int64_t* off, hipStream_t s);
+hipError_t launch_paged(int fmt, int h, int d, int clean, const PagedParams& p, hipStream_t s);
+hipError_t launch_paged_metadata(const int32_t* ctx, int32_t batch, int32_t bs, int32_t max_ctx,
+                                 int32_t num_splits, int32_t* sched, hipStream_t s);
+
+}  // namespace mqa

@@ -1,0 +1,241 @@
+// Paged decode weighted MQA logits and its work-split metadata for gfx950.
+//
+// The paged path of "How to Implement MQA (Multi-Query Attention) Logits
+// Computation with DeepGEMM" (Implementing Paged MQA Logits Computation for
+// Decoding): KV lives in fixed-size physical blocks reached through a block
+// table, each sequence has next_n new query tokens ("[PR #314] fix: SM90
+// paged MQA logits IMA on next_n=4", commit 12cb7c0), and a metadata call
+// made once per decoding step splits the (sequence, KV block) work list over
+// the workers (same PR, a97b74d Root cause / Fix).
+//
+// A worker is one wave.  Its 4 query rows are the next_n (<= 4) tokens of the
+// sequence it is on, so one unit = one KV block for all of a sequence's rows
+// (a single query atom: producer and consumer of the schedule cannot
+// disagree on atoms).  Columns past a sequence's last block are -inf fill
+// units spread round-robin over the workers in the same launch.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mqa {
+
+template <int FMT, int H, int D, bool CLEAN>
+__global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
+  using RG = RowGroup<FMT, H, D>;
+  using L = OperandLayout<FMT, D>;
+  constexpr int kNKB = RG::kNKB;
+  constexpr int kRowBytes = RG::kRowBytes;
+  constexpr int kBtWindow = kWaveLanes;        // block-table entries held per lane
+
+  const int lane = threadIdx.x & (kWaveLanes - 1);
+  const int worker = blockIdx.x;                // one wave per block
+  if (worker >= p.num_splits) return;
+
+  const int g = lane >> 4;                 // output row (query token) of this lane
+  const int n = lane & 15;                 // column within a 16-token tile
+  const int kb = lane >> 4;                // lane group: operand pieces and scale block
+  const bool kb_ok = L::scale_ok(kb);
+  const bool row_ok = g < p.next_n;
+  const int t_e = min(g, p.next_n - 1);
+  const int t_a = min((lane >> 2) & 3, p.next_n - 1);
+  const int bs = p.bs;
+  const int bs_shift = 31 - __builtin_clz(bs);
+
+  // operand lanes: token n of the step, the lane group's two 16-byte pieces
+  const int b_lo = L::lo(kb) >= 0 ? n * kRowBytes + L::lo(kb) : kOOB;
+  const int b_hi = L::hi(kb) >= 0 ? n * kRowBytes + L::hi(kb) : kOOB;
+  const int64_t pool_tokens = (int64_t)p.num_blocks * bs;
+  Rsrc sc_r;
+  if constexpr (FmtInfo<FMT>::kMX) {
+    sc_r = make_rsrc(p.kv_sf, (uint32_t)(pool_tokens * kNKB));
+  } else {
+    sc_r = make_rsrc(p.kv_scale, (uint32_t)(pool_tokens * 4));
+  }
+
+  int b = max(p.sched[2 * worker], 0);
+  int blk = max(p.sched[2 * worker + 1], 0);
+  const int eb = p.sched[2 * worker + 2];
+  const int eblk = p.sched[2 * worker + 3];
+
+  RG rg;
+  while (b < p.batch && (b < eb || (b == eb && blk < eblk))) {
+    const int ctx = p.ctx[b];
+    const int len = clampi(ctx, 0, p.max_ctx);
+    const int n_b = (len + bs - 1) >> bs_shift;
+    if (blk >= n_b) {                      // past this sequence: next one
+      ++b;
+      blk = 0;
+      continue;
+    }
+    // this worker's blocks of sequence b: [blk, seg_end)
+    const int seg_end = b < eb ? n_b : min(n_b, eblk);
+    const int64_t r0 = (int64_t)b * p.next_n;
+    rg.load(p.q, p.q_sf, p.w, r0 + t_a, r0 + t_e, lane);
+    const int e_tok = clampi(ctx - p.next_n + t_e + 1, 0, len);   // this lane's row end
+    const Rsrc out_r = make_rsrc(p.out + r0 * p.stride,
+                                 (uint32_t)(p.next_n * p.stride * 4));
+    const int lane_off = (t_e * (int)p.stride + n) * 4;
+    const int rel_n = n - e_tok;           // j0 + rel_n < 0  iff  column in range
+
+    for (int sub = blk; sub < seg_end; sub += kBtWindow) {
+      const int cnt = min(kBtWindow, seg_end - sub);
+      const int bt_lane = clampi(p.bt[(int64_t)b * p.bt_stride + sub + min(lane, cnt - 1)], 0,
+                                 p.num_blocks - 1);
+      const int col0 = sub << bs_shift;
+      const int col1 = min((sub + cnt) << bs_shift, p.max_ctx);
+      const int wlim_n = (row_ok ? col1 : 0) - n;
+
+      auto load = [&](int j0, KvOp& o) {
+        const int bi = min((j0 >> bs_shift) - sub, cnt - 1);
+        const int pblk = __builtin_amdgcn_readlane(bt_lane, bi);
+        const int tok = (pblk << bs_shift) + (j0 & (bs - 1));   // first pool token of the step
+        const Rsrc kv_r = make_rsrc(p.kv + (int64_t)tok * kRowBytes, kTileN * kRowBytes);
+        o.b = buffer_operand(kv_r, b_lo, b_hi);
+        if constexpr (FmtInfo<FMT>::kMX) {
+          o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, (tok + n) * kNKB + kb, 0, 0)
+                       : 127;
+          o.ks = 1.f;
+        } else {
+          o.bs = 127;
+          o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, (tok + n) * 4, 0, 0));
+        }
+      };
+      auto store = [&](int j0, float v) {
+        const bool in_range = j0 + rel_n < 0;
+        if constexpr (CLEAN) {
+          buffer_store_nt(out_r, j0 < wlim_n ? lane_off + 4 * j0 : kOOB, in_range ? v : neg_inf());
+        } else {
+          buffer_store_nt(out_r, (j0 < wlim_n && in_range) ? lane_off + 4 * j0 : kOOB, v);
+        }
+      };
+
+      // Paged decode is bound by the KV gather, so FP8 always takes the
+      // sign-exact path (negative token scales negate the token's codes)
+      // instead of scanning the scales first.
+      compute_span<!FmtInfo<FMT>::kMX>(rg, col0, col1, load, store);
+    }
+    blk = seg_end;
+  }
+
+  if constexpr (CLEAN) {
+    // -inf for the blocks past each sequence's last one, round-robin.
+    const int64_t total = (int64_t)p.batch * p.nb_max;
+    for (int64_t f = worker; f < total; f += p.num_splits) {
+      const int fb = (int)(f / p.nb_max);
+      const int c = (int)(f - (int64_t)fb * p.nb_max);
+      const int len = clampi(p.ctx[fb], 0, p.max_ctx);
+      if (c < ((len + bs - 1) >> bs_shift)) continue;
+      const Rsrc out_r = make_rsrc(p.out + (int64_t)fb * p.next_n * p.stride,
+                                   (uint32_t)(p.next_n * p.stride * 4));
+      const int lane_off = (t_e * (int)p.stride + n) * 4;
+      const int c1 = min((c + 1) << bs_shift, p.max_ctx);
+      for (int j0 = c << bs_shift; j0 < c1; j0 += kTileN)
+        buffer_store_nt(out_r, (row_ok && j0 + n < c1) ? lane_off + 4 * j0 : kOOB, neg_inf());
+    }
+  }
+}
+
+template <int FMT, int H, int D>
+static hipError_t launch_paged_inst(int clean, const PagedParams& p, hipStream_t s) {
+  const int grid = (p.num_splits + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (clean) {
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int H>
+static hipError_t paged_d(int d, int clean, const PagedParams& p, hipStream_t s) {
+  return d == 64 ? launch_paged_inst<FMT, H, 64>(clean, p, s)
+                 : launch_paged_inst<FMT, H, 128>(clean, p, s);
+}
+
+template <int FMT>
+static hipError_t paged_h(int h, int d, int clean, const PagedParams& p, hipStream_t s) {
+  switch (h) {
+    case 8: return paged_d<FMT, 8>(d, clean, p, s);
+    case 16: return paged_d<FMT, 16>(d, clean, p, s);
+    case 32: return paged_d<FMT, 32>(d, clean, p, s);
+    default: return paged_d<FMT, 64>(d, clean, p, s);
+  }
+}
+
+hipError_t launch_paged(int fmt, int h, int d, int clean, const PagedParams& p, hipStream_t s) {
+  switch (fmt) {
+    case kFP8: return paged_h<kFP8>(h, d, clean, p, s);
+    case kMXFP8: return paged_h<kMXFP8>(h, d, clean, p, s);
+    default: return paged_h<kMXFP4>(h, d, clean, p, s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Metadata: prefix sum of the per-sequence unit counts, then the first unit
+// of each of the num_splits even pieces, located by binary search.
+// ---------------------------------------------------------------------------
+constexpr int kMetaThreads = 1024;
+constexpr int kMetaMaxBatch = 8192;
+
+__global__ __launch_bounds__(kMetaThreads) void paged_metadata_kernel(
+    const int32_t* __restrict__ ctx, int32_t batch, int32_t bs, int32_t max_ctx,
+    int32_t num_splits, int32_t* __restrict__ sched) {
+  __shared__ int32_t prefix[kMetaMaxBatch + 1];
+  __shared__ int32_t part[kMetaThreads];
+  const int t = threadIdx.x;
+  constexpr int kPer = kMetaMaxBatch / kMetaThreads;   // sequences per thread
+  int local[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = t * kPer + k;
+    int nb = 0;
+    if (b < batch) {
+      const int len = clampi(ctx[b], 0, max_ctx);
+      nb = (len + bs - 1) / bs;
+    }
+    local[k] = nb;
+    sum += nb;
+  }
+  part[t] = sum;
+  __syncthreads();
+  for (int step = 1; step < kMetaThreads; step <<= 1) {   // inclusive scan
+    const int v = t >= step ? part[t - step] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = t * kPer + k;
+    if (b <= batch) prefix[b] = run;
+    run += local[k];
+  }
+  if (t == kMetaThreads - 1 && batch == kMetaMaxBatch) prefix[batch] = part[t];
+  __syncthreads();
+  const int64_t total = prefix[batch];
+  for (int c = t; c <= num_splits; c += kMetaThreads) {
+    const int64_t u = (int64_t)c * total / num_splits;
+    int sb = batch, sblk = 0;
+    if (u < total) {
+      int lo = 0, hi = batch;              // largest b with prefix[b] <= u
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (prefix[mid] <= u) lo = mid; else hi = mid;
+      }
+      sb = lo;
+      sblk = (int)(u - prefix[lo]);
+    }
+    sched[2 * c] = sb;
+    sched[2 * c + 1] = sblk;
+  }
+}
+
+hipError_t launch_paged_metadata(const int32_t* ctx, int32_t batch, int32_t bs, int32_t max_ctx,
+                                 int32_t num_splits, int32_t* sched, hipStream_t s) {
+  hipLaunchKernelGGL(paged_metadata_kernel, dim3(1), dim3(kMetaThreads), 0, s, ctx, batch, bs,
+                     max_ctx, num_splits, sched);
+  return hipGetLastError();
+}
+
+}  // namespace mqa

@@ -1,0 +1,158 @@
+"""The C-ABI library on a host without a GPU (CPU only).
+
+Checks that libmqa_logits.so loads, exports every function include/mqa_logits.h
+declares, rejects bad arguments on the host before any HIP call, and reports
+a missing device as MQA_ERR_HIP.  No test here reaches a kernel launch: every
+call with fake pointers is built to fail validation first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_logits.h")
+
+mq = pytest.importorskip("mqa_logits_amd")
+lib = mq.lib
+
+OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)          # aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x100004)      # 4- but not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"defined", "if", "extern"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ["mqa_logits", "mqa_logits_compressed", "mqa_logits_compressed_offsets",
+               "paged_mqa_logits", "paged_mqa_logits_metadata",
+               "paged_mqa_logits_metadata_size", "mqa_num_cus", "mqa_last_error",
+               "paged_mqa_logits_default_splits"]:
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported():
+    raw = ctypes.CDLL(mq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} is declared but not exported"
+    assert set(mq.EXPORTED) <= set(declared_functions())
+
+
+def dense_args(**kw):
+    a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kv_scale=FAKE, w=FAKE,
+             ks=FAKE, ke=FAKE, out=FAKE, stride=64, sq=16, skv=64, h=64, d=128, clean=1,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(h=48), UNSUPPORTED),
+    (dict(h=128), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED),
+    (dict(dt=7), INVALID),
+    (dict(q=None), INVALID),
+    (dict(kv=None), INVALID),
+    (dict(w=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(ks=None), INVALID),
+    (dict(q=FAKE_ODD), INVALID),
+    (dict(kv_scale=None), INVALID),                 # FP8 needs a token scale
+    (dict(q_sf=FAKE), INVALID),                     # FP8 takes no block scales
+    (dict(dt=1), INVALID),                          # MX needs block scales ...
+    (dict(dt=1, q_sf=FAKE, kv_sf=FAKE), INVALID),   # ... and takes no kv_scale
+    (dict(stride=63), INVALID),
+    (dict(sq=-1), INVALID),
+    (dict(skv=-5), INVALID),
+    (dict(stride=1 << 28), UNSUPPORTED),
+])
+def test_dense_validation_fails_before_any_launch(change, expect):
+    assert lib.mqa_logits(*dense_args(**change)) == expect
+    assert lib.mqa_last_error()
+
+
+def test_empty_problems_are_noops():
+    assert lib.mqa_logits(*dense_args(sq=0)) == OK
+    assert lib.mqa_logits(*dense_args(skv=0, stride=0)) == OK
+    assert lib.mqa_logits_compressed(0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 0, 64, 64, 128, None) == OK
+
+
+def test_compressed_validation():
+    base = [0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 64, 128, None]
+    bad = list(base)
+    bad[9] = None                                   # row_offsets
+    assert lib.mqa_logits_compressed(*bad) == INVALID
+    bad = list(base)
+    bad[13] = 40                                    # H
+    assert lib.mqa_logits_compressed(*bad) == UNSUPPORTED
+    assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, -1, 10, FAKE, None) == INVALID
+    assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, 4, 10, None, None) == INVALID
+
+
+def paged_meta_args(**kw):
+    a = dict(ctx=FAKE, batch=64, next_n=4, bs=64, max_ctx=32768, splits=256, sched=FAKE,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(batch=0), UNSUPPORTED),
+    (dict(batch=9000), UNSUPPORTED),
+    (dict(next_n=5), UNSUPPORTED),
+    (dict(next_n=0), UNSUPPORTED),
+    (dict(bs=128), UNSUPPORTED),
+    (dict(bs=48), UNSUPPORTED),
+    (dict(splits=0), INVALID),
+    (dict(max_ctx=-1), INVALID),
+    (dict(ctx=None), INVALID),
+    (dict(sched=None), INVALID),
+])
+def test_paged_metadata_validation(change, expect):
+    assert lib.paged_mqa_logits_metadata(*paged_meta_args(**change)) == expect
+
+
+def paged_args(**kw):
+    a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kvs=FAKE, w=FAKE, ctx=FAKE,
+             bt=FAKE, bt_stride=512, sched=FAKE, out=FAKE, stride=32768, batch=64, next_n=4,
+             h=64, d=128, bs=64, num_blocks=36000, max_ctx=32768, splits=1024, clean=1,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(bt_stride=511), INVALID),
+    (dict(stride=32767), INVALID),
+    (dict(num_blocks=0), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(sched=None), INVALID),
+    (dict(h=24), UNSUPPORTED),
+    (dict(next_n=6), UNSUPPORTED),
+    (dict(kvs=None), INVALID),
+])
+def test_paged_validation(change, expect):
+    assert lib.paged_mqa_logits(*paged_args(**change)) == expect
+
+
+def test_metadata_size():
+    assert lib.paged_mqa_logits_metadata_size(256) == 2 * 257
+    assert lib.paged_mqa_logits_metadata_size(0) == -1
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
+def test_missing_device_is_reported_as_hip_error():
+    assert lib.mqa_num_cus(0) < 0
+    assert "device" in lib.mqa_last_error().decode().lower()
+    with pytest.raises(mq.MqaError):
+        mq.mqa_num_cus(0)
