@@ -37,7 +37,7 @@ class MqaError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m mqa_logits_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python mqa_logits_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64

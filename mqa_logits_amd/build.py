@@ -1,6 +1,8 @@
 """Build libmqa_logits.so in-tree with hipcc for gfx950.
 
-Usage: python -m mqa_logits_amd.build   (or build() from Python)
+Usage: python mqa_logits_amd/build.py   (or __graft_entry__.build())
+
+Run it by path: importing the package loads the library this script makes.
 
 Every call recompiles.  Objects go to mqa_logits_amd/_build/, the shared
 library to mqa_logits_amd/libmqa_logits.so.

@@ -78,15 +78,17 @@ mqa_status check_common(mqa_dtype dt, const void* q, const uint8_t* q_sf, const 
 // Columns per block: enough blocks to give every compute unit several, with
 // chunks of at least 256 tokens.  Any multiple of 16 is correct.
 int32_t pick_chunk(int32_t sq, int32_t skv) {
+  // Enough (row group, chunk) blocks to give every SIMD a few, with chunks a
+  // whole number of pipeline trips wide so only a row's last chunk is ragged.
+  constexpr int64_t kTargetBlocks = 2048;
+  constexpr int64_t kTrip = 16 * mqa::kKvStages;
   const int64_t qblocks = (sq + 3) / 4;          // one wave (block) per 4 rows
-  const int64_t target_blocks = 8192;
-  int64_t n_chunks = (target_blocks + qblocks - 1) / qblocks;
+  int64_t n_chunks = (kTargetBlocks + qblocks - 1) / qblocks;
   const int64_t max_chunks = (skv + 255) / 256;
   if (n_chunks > max_chunks) n_chunks = max_chunks;
   if (n_chunks < 1) n_chunks = 1;
   int64_t cols = (skv + n_chunks - 1) / n_chunks;
-  cols = (cols + 15) & ~int64_t(15);
-  if (cols < 16) cols = 16;
+  cols = (cols + kTrip - 1) / kTrip * kTrip;
   return (int32_t)cols;
 }
 

@@ -70,12 +70,34 @@ __device__ __forceinline__ v8i make_op(uint4 a, uint4 b) {
 }
 
 template <int FMT>
-__device__ __forceinline__ v4f mma(const v8i& a, const v8i& b, int scale_a, int scale_b) {
+__device__ __forceinline__ v4f mma(const v8i& a, const v8i& b, int scale_a, int scale_b,
+                                   v4f c = v4f{0.f, 0.f, 0.f, 0.f}) {
   constexpr int f = FmtInfo<FMT>::kCode;
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, f, f, 0, scale_a, 0,
-                                                          scale_b);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, f, f, 0, scale_a, 0, scale_b);
 }
+
+// The matrix core adds the eight fp8 products that share an 8-byte piece of
+// an operand in a narrow fixed-point window below the largest of them
+// (measured: a product 2^-12 below the largest survives, 2^-15 is lost)
+// before accumulating in fp32.  With few heads that rounding can exceed the
+// tolerance of the weighted head sum, so for H <= 16 the fp8 formats run
+// "split": A is issued eight times, copy k keeping only byte k of every
+// 8-byte piece.  Each piece then holds one nonzero product, which is exact,
+// and the partial products chain through the fp32 accumulator.  (fp4
+// products are short enough to be exact in that window already.)
+template <int FMT, int H>
+struct Split {
+  static constexpr int kWays = (FMT != kMXFP4 && H <= 16) ? 8 : 1;
+  __device__ static v8i part(const v8i& a, int k) {
+    if constexpr (kWays == 1) {
+      return a;
+    } else {
+      const int me = k < 4 ? 0xff << (8 * k) : 0;         // even dwords: bytes 0..3 of a piece
+      const int mo = k < 4 ? 0 : 0xff << (8 * (k - 4));   // odd dwords: bytes 4..7
+      return v8i{a[0] & me, a[1] & mo, a[2] & me, a[3] & mo, a[4] & me, a[5] & mo, a[6] & me, a[7] & mo};
+    }
+  }
+};
 
 // Flip the sign of every e4m3 element of an operand (exact negation).
 __device__ __forceinline__ v8i negate_fp8(const v8i& b, int mask) {
@@ -114,6 +136,13 @@ __device__ __forceinline__ void buffer_store_nt(Rsrc r, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, off, 0, kNT);
 }
 
+// 16 bytes (4 consecutive fp32 columns) at off; kOOB drops the store.
+__device__ __forceinline__ void buffer_store4_nt(Rsrc r, int off, float4 v) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i x = {__float_as_int(v.x), __float_as_int(v.y), __float_as_int(v.z), __float_as_int(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kNT);
+}
+
 // Per-wave state of the 4 query rows a wave owns: the A operands (Q) with
 // their block scales, and this lane's weights.  H heads -> H/4 M tiles.
 template <int FMT, int H, int D>
@@ -122,7 +151,8 @@ struct RowGroup {
   static constexpr int kNKB = D / 32;                       // e8m0 blocks per row
   static constexpr int kRowBytes = OperandLayout<FMT, D>::kRowBytes;  // bytes per row
 
-  v8i qa[kMT];
+  static constexpr int kWays = Split<FMT, H>::kWays;
+  v8i qa[kMT * kWays];                                      // tile m, part k at m * kWays + k
   int qs[kMT];
   float w[H];
 
@@ -142,7 +172,9 @@ struct RowGroup {
       const uint8_t* row = q + hr * L::kRowBytes;
       const uint4 a = lo >= 0 ? *reinterpret_cast<const uint4*>(row + lo) : zero4();
       const uint4 b = hi >= 0 ? *reinterpret_cast<const uint4*>(row + hi) : zero4();
-      qa[m] = make_op(a, b);
+      const v8i op = make_op(a, b);
+#pragma unroll
+      for (int k = 0; k < kWays; ++k) qa[m * kWays + k] = Split<FMT, H>::part(op, k);
       if constexpr (FmtInfo<FMT>::kMX) {
         qs[m] = L::scale_ok(g) ? (int)q_sf[hr * L::kBlocks + g] : 127;
       } else {
@@ -153,7 +185,7 @@ struct RowGroup {
     // the MFMAs, which take A from AGPRs: keep them there and leave the VGPRs
     // to the accumulators, weights and streamed KV operands.
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) asm volatile("" : "+a"(qa[m]));
+    for (int m = 0; m < kMT * kWays; ++m) asm volatile("" : "+a"(qa[m]));
     const float4* wp = reinterpret_cast<const float4*>(wts + e_row * H);
 #pragma unroll
     for (int i = 0; i < H / 4; ++i) {
@@ -165,54 +197,60 @@ struct RowGroup {
     }
   }
 
-  // Software pipeline over 16-token steps.  acc holds the MFMA results of
-  // the step being consumed; consume_and_issue() reduces them tile by tile
-  // and, right behind each tile's VALU work, issues that tile's MFMA for the
-  // next step into the same registers, so the matrix core runs the next
-  // step while the VALU finishes this one.
-  v4f acc[kMT];
+  // Software pipeline over 16-token steps.  Tile m of a step lands in
+  // acc[m % kRing]; the VALU reduces the tile kLag slots behind the MFMA
+  // being issued, so a result is read about kLag MFMAs after its issue and
+  // only kRing tiles of accumulators are live.  s[] is the running weighted
+  // ReLU sum of the step being reduced.
+  static constexpr int kRing = kMT < 4 ? kMT : 4;
+  static constexpr int kLag = kRing / 2;
+  v4f acc[kRing];
+  float s[4];
 
-  __device__ __forceinline__ void issue(const v8i& b, int scale_b) {
+  __device__ __forceinline__ void start() {
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) acc[m] = mma<FMT>(qa[m], b, qs[m], scale_b);
+    for (int r = 0; r < kRing; ++r) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = 0.f;
   }
 
-  // sum_h w[h] * max(S[h], 0) for this lane's (row, token) of the consumed
-  // step; then acc <- the next step's products (operand b_next).
-  __device__ __forceinline__ float consume_and_issue(const v8i& b_next, int scale_b) {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  // sum_h w[h] * max(S[h], 0) over the 4 heads of tile mc (this lane's row
+  // and token), added to s[].
+  __device__ __forceinline__ void reduce_tile(int mc, const v4f& c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(w[4 * mc + i], __builtin_fmaxf(c[i], 0.f), s[i]);
+  }
+
+  __device__ __forceinline__ float take() {
+    const float v = (s[0] + s[1]) + (s[2] + s[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = 0.f;
+    return v;
+  }
+
+  // One step: issue its kMT MFMAs (operand b) while reducing the tiles kLag
+  // behind; once the previous step's last tile is reduced (slot kLag - 1),
+  // done(total of the previous step) runs.
+  template <class Done>
+  __device__ __forceinline__ void step(const v8i& b, int scale_b, Done&& done) {
 #pragma unroll
     for (int m = 0; m < kMT; ++m) {
-      const v4f c = acc[m];
-      s0 = __builtin_fmaf(w[4 * m + 0], __builtin_fmaxf(c[0], 0.f), s0);
-      s1 = __builtin_fmaf(w[4 * m + 1], __builtin_fmaxf(c[1], 0.f), s1);
-      s2 = __builtin_fmaf(w[4 * m + 2], __builtin_fmaxf(c[2], 0.f), s2);
-      s3 = __builtin_fmaf(w[4 * m + 3], __builtin_fmaxf(c[3], 0.f), s3);
-      acc[m] = mma<FMT>(qa[m], b_next, qs[m], scale_b);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then 1 MFMA
-    }
-    return (s0 + s1) + (s2 + s3);
-  }
-
-  // The same reduction with no next step to issue.
-  __device__ __forceinline__ float consume() const {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      reduce_tile((m - kLag + kMT) % kMT, acc[(m - kLag + kRing) % kRing]);
+      v4f c = mma<FMT>(qa[m * kWays], b, qs[m], scale_b);
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) {
-      const v4f c = acc[m];
-      s0 = __builtin_fmaf(w[4 * m + 0], __builtin_fmaxf(c[0], 0.f), s0);
-      s1 = __builtin_fmaf(w[4 * m + 1], __builtin_fmaxf(c[1], 0.f), s1);
-      s2 = __builtin_fmaf(w[4 * m + 2], __builtin_fmaxf(c[2], 0.f), s2);
-      s3 = __builtin_fmaf(w[4 * m + 3], __builtin_fmaxf(c[3], 0.f), s3);
+      for (int k = 1; k < kWays; ++k) c = mma<FMT>(qa[m * kWays + k], b, qs[m], scale_b, c);
+      acc[m % kRing] = c;
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);       // 8 VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, kWays, 0);   // then the tile's MFMAs
+      if (m == kLag - 1) done(take());
     }
-    return (s0 + s1) + (s2 + s3);
   }
 
-  // Non-pipelined: products and reduction of one step.
-  __device__ __forceinline__ float weighted_relu_sum(const v8i& b, int scale_b) {
-    issue(b, scale_b);
-    return consume();
+  // The last kLag tiles of the final step (no MFMA left): its total.
+  __device__ __forceinline__ float drain() {
+#pragma unroll
+    for (int k = 0; k < kLag; ++k) reduce_tile(kMT - kLag + k, acc[(kMT - kLag + k) % kRing]);
+    return take();
   }
 };
 
@@ -224,47 +262,72 @@ struct KvOp {
   float ks;
 };
 
-// Walk the 16-token steps from cl of one wave, software-pipelined: at the
-// top of iteration j0 the accumulators hold the products of step j0 and the
-// operand of step j0 + 16 has been in flight for two iterations.  The
-// iteration reduces step j0 while issuing step j0 + 16's MFMAs, prefetches
-// step j0 + 48, and hands (j0, value) to store(j0, v).  The three operand
-// buffers rotate by name, three steps per trip, and the step count is padded
-// to a multiple of three so the back-edge is the only branch (an exit inside
-// the trip would let the compiler sink the next step's MFMAs behind it).
-// load(j0, KvOp&) must zero-fill tokens past the KV range and store() must
-// drop columns past the chunk.  Returns the first column not walked.
-template <bool FLIP, class RG, class Load, class StoreFn>
-__device__ __forceinline__ int compute_span(RG& rg, int cl, int ch, Load&& load, StoreFn&& store) {
-  auto prep = [&](KvOp& o) {
-    if constexpr (FLIP) o.b = negate_fp8(o.b, o.ks < 0.f ? (int)0x80808080 : 0);
-  };
+// Walk the 16-token steps from cl of one wave.  The KV operands ride a ring
+// of kKvStages slots, slot k holding the steps k, k + kKvStages, ... of the
+// walk.  A step's total is known kLag tiles into the next step: it goes to
+// sink.put(u, j0, v), u = the position of step j0 in its trip of kKvStages
+// steps, and sink.trip(jt) follows the put of trip jt's last step.  Once that
+// put has read the previous step's token scale, its slot is refilled with the
+// step kKvStages further on, which is then kKvStages - 1 steps ahead of its
+// MFMAs.  Each loop iteration is one trip with the ring rotating by name and
+// the step count padded to whole trips, so the back-edge is the only branch
+// (an exit inside the trip would let the compiler sink MFMAs behind it) and
+// no loaded value is copied between registers (a copy would wait for its
+// load).  The very first put is for the phantom step cl - 16 (a zero value):
+// sinks drop columns below cl.  load(j0, KvOp&) must zero-fill tokens past
+// the KV range and the sink must drop columns past the caller's range.
+// Returns the first column not walked.
+template <bool FLIP, class RG, class Load, class Sink>
+__device__ __forceinline__ int compute_span(RG& rg, int cl, int ch, Load&& load, Sink& sink) {
+  constexpr int S = kKvStages;
   const int steps = (ch - cl + kTileN - 1) / kTileN;
-  const int end = cl + (steps + 2) / 3 * 3 * kTileN;
-  KvOp o0, o1, o2;
-  load(cl, o0);
-  load(cl + kTileN, o1);
-  load(cl + 2 * kTileN, o2);
-  prep(o0);
-  rg.issue(o0.b, o0.bs);
-  float ks_prev = o0.ks;                       // token scale of the step in acc
+  const int end = cl + (steps + S - 1) / S * S * kTileN;
+  KvOp o[S];
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u) load(cl + u * kTileN, o[u]);
+  o[S - 1].ks = 0.f;                           // the phantom step cl - 16
+  rg.start();
 
-  auto body = [&](int j0, KvOp& use, KvOp& ld) {
-    const float ks_j0 = ks_prev;
-    ks_prev = use.ks;
-    load(j0 + 3 * kTileN, ld);                 // ld held step j0, already issued
-    prep(use);
-    float v = rg.consume_and_issue(use.b, use.bs);
-    v *= __builtin_fabsf(ks_j0);
-    asm volatile("" : "+v"(v));                // keep the reduction ahead of the store
-    store(j0, v);
-  };
-  for (int j0 = cl; j0 < end; j0 += 3 * kTileN) {
-    body(j0, o1, o0);
-    body(j0 + kTileN, o2, o1);
-    body(j0 + 2 * kTileN, o0, o2);
+  for (int j0 = cl; j0 < end; j0 += S * kTileN) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      KvOp& cur = o[u];                        // step j0 + 16 u
+      KvOp& prv = o[(u + S - 1) % S];          // step j0 + 16 (u - 1), finished in this one
+      if constexpr (FLIP) cur.b = negate_fp8(cur.b, cur.ks < 0.f ? (int)0x80808080 : 0);
+      rg.step(cur.b, cur.bs, [&](float v) {
+        v *= __builtin_fabsf(prv.ks);
+        asm volatile("" : "+v"(v));            // keep the reduction ahead of the store
+        sink.put((u + S - 1) % S, j0 + (u - 1) * kTileN, v);
+      });
+      if (u == 0) sink.trip(j0 - S * kTileN);
+      load(j0 + (u - 1 + S) * kTileN, prv);
+      // keep the refill here: sunk towards its use it would leave a single
+      // step to cover the load latency
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  float v = rg.drain() * __builtin_fabsf(o[S - 1].ks);   // the last step sits in slot S - 1
+  asm volatile("" : "+v"(v));
+  sink.put(S - 1, end - kTileN, v);
+  sink.trip(end - S * kTileN);
+  sink.finish();
   return end;
 }
+
+// Sink that stores every step's value straight to its output column with a
+// 4-byte store (a per-lane offset of kOOB drops it).
+template <class OffFn>
+struct DwordSink {
+  Rsrc r;
+  OffFn off;                                   // (j0, &v) -> byte offset or kOOB; may edit v
+  int lo_j0;                                   // steps below lo_j0 are dropped
+  __device__ __forceinline__ void put(int, int j0, float v) {
+    int o = off(j0, v);
+    o = j0 >= lo_j0 ? o : kOOB;
+    buffer_store_nt(r, o, v);
+  }
+  __device__ __forceinline__ void trip(int) {}
+  __device__ __forceinline__ void finish() {}
+};
 
 }  // namespace mqa

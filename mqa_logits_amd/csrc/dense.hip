@@ -20,6 +20,44 @@
 
 namespace mqa {
 
+constexpr int kTripCols = kTileN * kKvStages;  // columns per pipeline trip
+
+// Clean dense output.  A trip's 4 rows x kTripCols columns are staged in LDS
+// and leave as one 16-byte store per lane (lane l: row l / 16, columns
+// 4 (l % 16) .. +3 of the trip), so every row gets whole 256-byte runs
+// instead of a 64-byte piece per step: HBM never has to fetch an output line
+// to merge a partial write.  Trips alternate between two LDS buffers; a
+// trip's group is read back right after its last put and stored one step
+// later, when the read has long returned.
+struct StagedSink {
+  float* stage;              // 2 x [4][kTripCols] floats in LDS
+  Rsrc r;
+  int base;                  // first column of the walk (trip-aligned)
+  int put_idx;               // this lane's slot: row g, column n of a trip's first step
+  int rd_idx;                // this lane's group: row l / 16, column 4 (l % 16)
+  int row_off;               // byte offset of this lane's group in the output, column 0
+  int last_j0;               // the group of trip j0 is stored iff base <= j0 <= last_j0
+  int rel_n, len;            // column j0 + n is in range iff j0 + rel_n in [0, len)
+  float4 pend;               // the last trip read back, and its store offset
+  int pend_off;
+
+  __device__ __forceinline__ float* buffer(int j0) const {
+    return stage + (((j0 - base) >> 6) & 1) * (kRowsPerWave * kTripCols);
+  }
+  __device__ __forceinline__ void put(int u, int j0, float v) {
+    const bool in_range = (uint32_t)(j0 + rel_n) < (uint32_t)len;
+    buffer(j0)[put_idx + u * kTileN] = in_range ? v : neg_inf();
+    if (u == 0) buffer_store4_nt(r, pend_off, pend);
+  }
+  __device__ __forceinline__ void trip(int jt) {
+    asm volatile("" ::: "memory");            // the group read follows every lane's writes
+    pend = *reinterpret_cast<const float4*>(buffer(jt) + rd_idx);
+    pend_off = (jt >= base && jt <= last_j0) ? row_off + 4 * jt : kOOB;
+    asm volatile("" ::: "memory");
+  }
+  __device__ __forceinline__ void finish() { buffer_store4_nt(r, pend_off, pend); }
+};
+
 template <int FMT, int H, int D, int STORE>
 __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   using RG = RowGroup<FMT, H, D>;
@@ -55,8 +93,6 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   const int s_row = clampi(p.k_start[e_row_c], 0, p.skv);
   int e_end = clampi(p.k_end[e_row_c], s_row, p.skv);
   if (!row_ok) e_end = s_row;
-  // stores stay inside this block's chunk [c0, c1) (set below)
-  int len;
 
   // Union of the 4 rows' ranges (wave-uniform).
   int lo = 0x7fffffff, hi = 0;
@@ -70,39 +106,30 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
     }
   }
 
+  // Chunks are whole trips wide, so c0 and cl below are trip-aligned.
   const int c0 = chunk * p.chunk_cols;
   const int c1 = min(c0 + p.chunk_cols, p.skv);
-  int cl = max(c0, lo & ~(kTileN - 1));
+  int cl = max(c0, lo & ~(kTripCols - 1));
   int ch = min(c1, hi);
   if (cl >= ch) { cl = c1; ch = c1; }          // nothing to compute in this chunk
-  len = max(0, min(e_end, c1) - s_row);
+  const int len = max(0, min(e_end, c1) - s_row);
+  const int rel_n = n - s_row;                 // (j0 + rel_n) in [0, len) iff in range
 
   // ---- output addressing: one buffer resource per wave -------------------
-  // byte offset of (this lane's row, column 0) inside the wave's region
   Rsrc out_r;
-  int lane_off;
+  int lane_off;                                // byte offset of (row g, column n), column 0
   if constexpr (STORE == kCompressed) {
     const int64_t first = p.row_off[row0];
     const int64_t last = p.row_off[min(row0 + kRowsPerWave, p.sq)];
     out_r = make_rsrc(p.out + first, (uint32_t)((last - first) * 4));
-    lane_off = (int)(row_ok ? (p.row_off[e_row_c] - first - s_row) * 4 : 0);
+    lane_off = (int)(row_ok ? (p.row_off[e_row_c] - first - s_row) * 4 : 0) + 4 * n;
   } else {
     const int rows = min(kRowsPerWave, p.sq - row0);
     out_r = make_rsrc(p.out + (int64_t)row0 * p.stride, (uint32_t)(rows * p.stride * 4));
-    lane_off = (int)(g * p.stride * 4);
-  }
-  lane_off += 4 * n;
-  // clean stores write columns [c0, c1) of valid rows, in-range or -inf
-  const int wlim_n = (row_ok ? c1 : 0) - n;    // column j0 + n is writable iff j0 < wlim_n
-  const int rel_n = n - s_row;                 // (j0 + rel_n) in [0, len) iff in range
-
-  // ---- -inf fill of whole tiles left of the computed span ----------------
-  if constexpr (STORE == kDenseClean) {
-    for (int j0 = c0; j0 < cl; j0 += kTileN)
-      buffer_store_nt(out_r, j0 < wlim_n ? lane_off + 4 * j0 : kOOB, neg_inf());
+    lane_off = (int)(g * p.stride * 4) + 4 * n;
   }
 
-  // ---- computed tiles ------------------------------------------------------
+  // ---- KV operands ---------------------------------------------------------
   // KV operand of lane l: token j0 + l % 16, the two 16-byte pieces of lane
   // group l / 16 (OperandLayout), and that group's e8m0 block scale (MX).
   const int kb = lane >> 4;
@@ -155,34 +182,53 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
     }
   }
 
-  int walked = ch;
-  if (cl < ch) {
-    if (flip) {
-      walked = compute_span<true>(rg, cl, ch, load_b, [&](int j0, float v) {
-        const bool in_range = (uint32_t)(j0 + rel_n) < (uint32_t)len;
-        if constexpr (STORE == kDenseClean) {
-          buffer_store_nt(out_r, j0 < wlim_n ? lane_off + 4 * j0 : kOOB, in_range ? v : neg_inf());
-        } else {
-          buffer_store_nt(out_r, in_range ? lane_off + 4 * j0 : kOOB, v);
-        }
-      });
-    } else {
-      walked = compute_span<false>(rg, cl, ch, load_b, [&](int j0, float v) {
-        const bool in_range = (uint32_t)(j0 + rel_n) < (uint32_t)len;
-        if constexpr (STORE == kDenseClean) {
-          buffer_store_nt(out_r, j0 < wlim_n ? lane_off + 4 * j0 : kOOB, in_range ? v : neg_inf());
-        } else {
-          buffer_store_nt(out_r, in_range ? lane_off + 4 * j0 : kOOB, v);
-        }
-      });
+  auto walk = [&](auto& sink) {
+    int walked = ch;
+    if (cl < ch) {
+      if (flip) walked = compute_span<true>(rg, cl, ch, load_b, sink);
+      else walked = compute_span<false>(rg, cl, ch, load_b, sink);
     }
-  }
+    return walked;
+  };
 
-  // ---- -inf fill of whole tiles right of the computed span ---------------
   if constexpr (STORE == kDenseClean) {
-    const int start = cl < ch ? walked : c1;
-    for (int j0 = start; j0 < c1; j0 += kTileN)
-      buffer_store_nt(out_r, j0 < wlim_n ? lane_off + 4 * j0 : kOOB, neg_inf());
+    __shared__ __attribute__((aligned(16))) float stage[2 * kRowsPerWave * kTripCols];
+    const int rows = min(kRowsPerWave, p.sq - row0);
+    const int col4 = 4 * n;                     // lane l's group: row g, columns col4 .. col4 + 3
+    const bool grp_ok = g < rows;
+    const int grp_off = (int)(g * p.stride * 4) + 4 * col4;
+    const int lim = c1 & ~3;
+    const float4 ninf4 = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+    // a group is stored when its row exists and it ends at or below lim
+    const int last_j0 = grp_ok ? lim - col4 - 4 : -0x40000000;
+    auto fill = [&](int from, int to) {          // -inf over whole trips [from, to)
+      for (int j0 = from; j0 < to; j0 += kTripCols)
+        buffer_store4_nt(out_r, j0 <= last_j0 ? grp_off + 4 * j0 : kOOB, ninf4);
+    };
+    fill(c0, cl);
+    StagedSink sink{stage, out_r, cl, g * kTripCols + n, g * kTripCols + col4, grp_off, last_j0,
+                    rel_n, len, ninf4, kOOB};
+    const int walked = walk(sink);
+    fill(cl < ch ? walked : c1, c1);
+    // The last group of a row whose Skv is not a multiple of 4: 1..3 columns,
+    // one per lane, from the last trip's LDS buffer or -inf.
+    if ((c1 & 3) != 0) {
+      const int gs = c1 & ~3;
+      if (row_ok && gs + n < c1) {
+        float v = neg_inf();
+        const int jt = walked - kTripCols;
+        if (cl < ch && gs >= jt && gs < walked) v = sink.buffer(jt)[g * kTripCols + (gs - jt) + n];
+        buffer_store_nt(out_r, (int)(g * p.stride * 4) + 4 * (gs + n), v);
+      }
+    }
+  } else {
+    // Keep and compressed: each in-range value goes straight to its column.
+    auto off = [&](int j0, float& v) {
+      (void)v;
+      return (uint32_t)(j0 + rel_n) < (uint32_t)len ? lane_off + 4 * j0 : kOOB;
+    };
+    DwordSink<decltype(off)> sink{out_r, off, cl};
+    walk(sink);
   }
 }
 

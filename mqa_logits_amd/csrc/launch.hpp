@@ -15,6 +15,10 @@ enum Store : int { kDenseClean = 0, kDenseKeep = 1, kCompressed = 2 };
 constexpr int kWavesPerBlock = 1;
 // Resident waves per compute unit the kernels are sized for (one per SIMD).
 constexpr int kWavesPerCu = 4;
+// KV operand buffers in flight per wave: a step's operands are requested
+// kKvStages - 1 steps (16 tokens each) before their MFMAs issue, and a wave
+// walks whole trips of kKvStages steps.
+constexpr int kKvStages = 4;
 
 struct DenseParams {
   const uint8_t* q;        // [Sq, H, D] bytes (fp4: D/2)
@@ -29,7 +33,7 @@ struct DenseParams {
   float* out;
   int64_t stride;          // dense row stride in elements
   int32_t sq, skv;
-  int32_t chunk_cols;      // KV columns per block, a multiple of 16
+  int32_t chunk_cols;      // KV columns per block, a multiple of 16 * kKvStages
   int32_t n_chunks;        // ceil(Skv / chunk_cols)
 };
 

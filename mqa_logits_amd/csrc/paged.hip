@@ -99,19 +99,21 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
           o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, (tok + n) * 4, 0, 0));
         }
       };
-      auto store = [&](int j0, float v) {
+      auto off = [&](int j0, float& v) {
         const bool in_range = j0 + rel_n < 0;
         if constexpr (CLEAN) {
-          buffer_store_nt(out_r, j0 < wlim_n ? lane_off + 4 * j0 : kOOB, in_range ? v : neg_inf());
+          v = in_range ? v : neg_inf();
+          return j0 < wlim_n ? lane_off + 4 * j0 : kOOB;
         } else {
-          buffer_store_nt(out_r, (j0 < wlim_n && in_range) ? lane_off + 4 * j0 : kOOB, v);
+          return (j0 < wlim_n && in_range) ? lane_off + 4 * j0 : kOOB;
         }
       };
+      DwordSink<decltype(off)> sink{out_r, off, col0};
 
       // Paged decode is bound by the KV gather, so FP8 always takes the
       // sign-exact path (negative token scales negate the token's codes)
       // instead of scanning the scales first.
-      compute_span<!FmtInfo<FMT>::kMX>(rg, col0, col1, load, store);
+      compute_span<!FmtInfo<FMT>::kMX>(rg, col0, col1, load, sink);
     }
     blk = seg_end;
   }
