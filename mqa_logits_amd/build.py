@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmqa_logits.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dense.hip", "paged.hip", "api.cpp"]
+SOURCES = ["dense.hip", "qsum.hip", "paged.hip", "api.cpp"]
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 COMMON_FLAGS = [

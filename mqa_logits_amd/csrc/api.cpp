@@ -121,7 +121,23 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   if (debug_enabled())
     fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d store=%d Sq=%d Skv=%d chunk=%d grid=%lld\n",
             who, (int)dt, h, d, store, sq, skv, p.chunk_cols, (long long)grid);
-  return hip_status(mqa::launch_dense((int)dt, h, d, store, p, stream), who);
+  if (h != mqa::kLinHeads)
+    return hip_status(mqa::launch_dense((int)dt, h, d, store, p, stream), who);
+
+  // H = 64: the weighted query sum's pieces live in a stream-ordered
+  // workspace for the duration of the call.
+  const size_t ql_bytes = (size_t)sq * 4 * d, sf_bytes = (size_t)sq * 4 * (d / 32);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, ql_bytes + sf_bytes + 16, stream);
+  if (e != hipSuccess) return hip_status(e, who);
+  mqa::QsumParams qp{p.q, q_sf, weights, static_cast<uint8_t*>(ws),
+                     static_cast<uint8_t*>(ws) + ql_bytes, sq};
+  p.ql = qp.ql;
+  p.ql_sf = qp.ql_sf;
+  e = mqa::launch_qsum((int)dt, d, qp, stream);
+  if (e == hipSuccess) e = mqa::launch_dense((int)dt, h, d, store, p, stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  return hip_status(e != hipSuccess ? e : ef, who);
 }
 
 }  // namespace

@@ -143,9 +143,22 @@ __device__ __forceinline__ void buffer_store4_nt(Rsrc r, int off, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kNT);
 }
 
+// The linear-half tile: A in e4m3 (the weighted query sum's pieces, with
+// their own block scales), B in the KV format.
+template <int FMT>
+__device__ __forceinline__ v4f mma_lin(const v8i& a, const v8i& b, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0,
+                                                          FmtInfo<FMT>::kCode, 0, scale_a, 0,
+                                                          scale_b);
+}
+
 // Per-wave state of the 4 query rows a wave owns: the A operands (Q) with
 // their block scales, and this lane's weights.  H heads -> H/4 M tiles.
-template <int FMT, int H, int D>
+// LIN: ReLU(x) = (|x| + x) / 2; the lane's weights are halved and reduce
+// |x|, and a 17th tile (A = the four pieces of each row's weighted query sum
+// q', rows (query r / 4, piece r % 4)) supplies the x / 2 half, so lane l's
+// four accumulators of that tile are the pieces of its own row.
+template <int FMT, int H, int D, bool LIN = false>
 struct RowGroup {
   static constexpr int kMT = H / 4;
   static constexpr int kNKB = D / 32;                       // e8m0 blocks per row
@@ -187,13 +200,34 @@ struct RowGroup {
 #pragma unroll
     for (int m = 0; m < kMT * kWays; ++m) asm volatile("" : "+a"(qa[m]));
     const float4* wp = reinterpret_cast<const float4*>(wts + e_row * H);
+    constexpr float kW = LIN ? 0.5f : 1.f;
 #pragma unroll
     for (int i = 0; i < H / 4; ++i) {
       float4 v = wp[i];
-      w[4 * i + 0] = v.x;
-      w[4 * i + 1] = v.y;
-      w[4 * i + 2] = v.z;
-      w[4 * i + 3] = v.w;
+      w[4 * i + 0] = kW * v.x;
+      w[4 * i + 1] = kW * v.y;
+      w[4 * i + 2] = kW * v.z;
+      w[4 * i + 3] = kW * v.w;
+    }
+  }
+
+  // LIN: the pieces of q' for A row (l % 16) = (query a_row, piece l % 4),
+  // laid out like an MXFP8 query with 4 heads.
+  v8i ql;
+  int qls;
+  __device__ __forceinline__ void load_lin(const uint8_t* __restrict__ qlp,
+                                           const uint8_t* __restrict__ ql_sf, int64_t a_row,
+                                           int lane) {
+    if constexpr (LIN) {
+      using L8 = OperandLayout<kFP8, D>;
+      const int g = lane >> 4;
+      const int64_t pr = a_row * 4 + (lane & 3);
+      const uint8_t* row = qlp + pr * D;
+      const uint4 a = L8::lo(g) >= 0 ? *reinterpret_cast<const uint4*>(row + L8::lo(g)) : zero4();
+      const uint4 b = L8::hi(g) >= 0 ? *reinterpret_cast<const uint4*>(row + L8::hi(g)) : zero4();
+      ql = make_op(a, b);
+      qls = L8::scale_ok(g) ? (int)ql_sf[pr * L8::kBlocks + g] : 127;
+      asm volatile("" : "+a"(ql));
     }
   }
 
@@ -204,21 +238,32 @@ struct RowGroup {
   // ReLU sum of the step being reduced.
   static constexpr int kRing = kMT < 4 ? kMT : 4;
   static constexpr int kLag = kRing / 2;
+  static constexpr int kValuPerTile = LIN ? 4 : 8;
   v4f acc[kRing];
+  v4f accl;                                    // LIN: the linear tile of the last step
   float s[4];
 
   __device__ __forceinline__ void start() {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    accl = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = 0.f;
   }
 
-  // sum_h w[h] * max(S[h], 0) over the 4 heads of tile mc (this lane's row
-  // and token), added to s[].
+  // sum_h w[h] * max(S[h], 0) (LIN: sum_h (w[h] / 2) |S[h]|) over the 4 heads
+  // of tile mc (this lane's row and token), added to s[].
   __device__ __forceinline__ void reduce_tile(int mc, const v4f& c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(w[4 * mc + i], __builtin_fmaxf(c[i], 0.f), s[i]);
+    for (int i = 0; i < 4; ++i) {
+      const float r = LIN ? __builtin_fabsf(c[i]) : __builtin_fmaxf(c[i], 0.f);
+      s[i] = __builtin_fmaf(w[4 * mc + i], r, s[i]);
+    }
+  }
+
+  // LIN: add the x / 2 half of the step whose linear tile is in accl.
+  __device__ __forceinline__ void add_lin() {
+    if constexpr (LIN) s[0] += (accl[0] + accl[1]) + (accl[2] + accl[3]);
   }
 
   __device__ __forceinline__ float take() {
@@ -240,9 +285,16 @@ struct RowGroup {
 #pragma unroll
       for (int k = 1; k < kWays; ++k) c = mma<FMT>(qa[m * kWays + k], b, qs[m], scale_b, c);
       acc[m % kRing] = c;
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);       // 8 VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, kWays, 0);   // then the tile's MFMAs
-      if (m == kLag - 1) done(take());
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerTile, 0);   // the reduction VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, kWays, 0);          // then the tile's MFMAs
+      if (m == kLag - 1) {
+        add_lin();
+        done(take());
+      }
+    }
+    if constexpr (LIN) {
+      accl = mma_lin<FMT>(ql, b, qls, scale_b);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   }
 
@@ -250,6 +302,7 @@ struct RowGroup {
   __device__ __forceinline__ float drain() {
 #pragma unroll
     for (int k = 0; k < kLag; ++k) reduce_tile(kMT - kLag + k, acc[(kMT - kLag + k) % kRing]);
+    add_lin();
     return take();
   }
 };

@@ -60,7 +60,7 @@ struct StagedSink {
 
 template <int FMT, int H, int D, int STORE>
 __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
-  using RG = RowGroup<FMT, H, D>;
+  using RG = RowGroup<FMT, H, D, H == kLinHeads>;
   using L = OperandLayout<FMT, D>;
   constexpr int kNKB = RG::kNKB;
   constexpr int kRowBytes = RG::kRowBytes;
@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
 
   RG rg;
   rg.load(p.q, p.q_sf, p.w, a_row_c, e_row_c, lane);
+  rg.load_lin(p.ql, p.ql_sf, a_row_c, lane);
 
   const int s_row = clampi(p.k_start[e_row_c], 0, p.skv);
   int e_end = clampi(p.k_end[e_row_c], s_row, p.skv);

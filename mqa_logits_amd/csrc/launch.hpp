@@ -35,6 +35,21 @@ struct DenseParams {
   int32_t sq, skv;
   int32_t chunk_cols;      // KV columns per block, a multiple of 16 * kKvStages
   int32_t n_chunks;        // ceil(Skv / chunk_cols)
+  const uint8_t* ql;       // [Sq, 4, D] e4m3 pieces of the weighted query sum (H = 64)
+  const uint8_t* ql_sf;    // [Sq, 4, D/32] their e8m0 scales
+};
+
+// Heads whose kernels split ReLU into |x| / 2 and x / 2 and take the linear
+// half from the weighted query sum (qsum.hip).
+constexpr int kLinHeads = 64;
+
+struct QsumParams {
+  const uint8_t* q;        // [Sq, H, D] codes (fp4: D/2 bytes per row)
+  const uint8_t* q_sf;     // [Sq, H, D/32] or null
+  const float* w;          // [Sq, H]
+  uint8_t* ql;             // [Sq, 4, D]
+  uint8_t* ql_sf;          // [Sq, 4, D/32]
+  int32_t sq;
 };
 
 struct PagedParams {
@@ -54,6 +69,7 @@ struct PagedParams {
 };
 
 hipError_t launch_dense(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
+hipError_t launch_qsum(int fmt, int d, const QsumParams& p, hipStream_t s);
 hipError_t launch_compressed_offsets(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
                                      int64_t* off, hipStream_t s);
 hipError_t launch_paged(int fmt, int h, int d, int clean, const PagedParams& p, hipStream_t s);

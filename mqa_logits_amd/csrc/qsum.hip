@@ -1,0 +1,109 @@
+// Weighted query sums for the linear half of the ReLU, gfx950.
+//
+// With H = 64 heads the dense kernels evaluate
+//   sum_h w[i,h] ReLU(x_h) = sum_h (w[i,h] / 2) |x_h| + sum_h (w[i,h] / 2) x_h,
+// ReLU(x) = (x + |x|) / 2, x_h = <q[i,h,:], kv[j,:]> (the weighted head sum of
+// "How to Implement MQA (Multi-Query Attention) Logits Computation with
+// DeepGEMM", Core Architecture Components).  The second sum is linear in kv:
+// it equals <q'_i, kv[j,:]> with q'_i = sum_h (w[i,h] / 2) q[i,h,:], so the
+// matrix core computes it as one extra 16-row tile per 16 tokens instead of a
+// max and an fma per head in the vector ALU.  This kernel forms q'_i in fp32
+// from the decoded codes (block scales applied) and writes it as four e4m3
+// pieces, each with one e8m0 scale per 32 elements, that sum to q'_i to about
+// 2^-16 of each block's largest magnitude:
+//   ql    [Sq][4][D]     e4m3 codes, piece p of row i at (i * 4 + p) * D
+//   ql_sf [Sq][4][D/32]  e8m0 block scales
+// -- the layout of an [Sq, 4, D] MXFP8 query tensor, so the dense kernels
+// load it like Q.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mqa {
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  const float v = e == 0 ? (float)m * 0x1p-9f : ldexpf(1.f + (float)m * 0.125f, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const int e = (c >> 1) & 3, m = c & 1;
+  const float v = e == 0 ? 0.5f * (float)m : ldexpf(1.f + 0.5f * (float)m, e - 1);
+  return (c & 8) ? -v : v;
+}
+
+// Nearest e4m3 code of x, ties to even; |x| <= 448.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t s = x < 0.f ? 0x80u : 0u;
+  const float a = fabsf(x);
+  if (a < 0x1p-6f) {                           // subnormals: multiples of 2^-9
+    const uint32_t m = (uint32_t)rintf(a * 0x1p9f);   // 8 is the smallest normal
+    return m ? (s | m) : 0u;
+  }
+  int e;
+  const float f = frexpf(a, &e);               // a = f 2^e, f in [0.5, 1)
+  uint32_t m = (uint32_t)rintf((2.f * f - 1.f) * 8.f);
+  int be = e - 1 + 7;                          // biased exponent of (1 + m/8) 2^(e-1)
+  if (m == 8) { m = 0; ++be; }
+  return s | ((uint32_t)be << 3) | m;
+}
+
+template <int FMT, int H, int D>
+__global__ __launch_bounds__(D) void qsum_kernel(QsumParams p) {
+  constexpr int kRowBytes = FMT == kMXFP4 ? D / 2 : D;
+  constexpr int kNKB = D / 32;
+  const int64_t i = blockIdx.x;
+  const int k = threadIdx.x;
+
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    const int64_t hr = i * H + h;
+    float v;
+    if constexpr (FMT == kMXFP4) {
+      const uint32_t b = p.q[hr * kRowBytes + (k >> 1)];
+      v = e2m1_value((k & 1) ? b >> 4 : b & 15u);
+    } else {
+      v = e4m3_value(p.q[hr * kRowBytes + k]);
+    }
+    if constexpr (FmtInfo<FMT>::kMX) v = ldexpf(v, (int)p.q_sf[hr * kNKB + (k >> 5)] - 127);
+    acc = __builtin_fmaf(0.5f * p.w[hr], v, acc);
+  }
+
+  // Four pieces: each takes the block's residual at the largest e8m0 scale
+  // that keeps every element within e4m3's range.
+  float r = acc;
+#pragma unroll
+  for (int piece = 0; piece < 4; ++piece) {
+    float m = fabsf(r);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));   // the 32-element block
+    int sc = -127;
+    if (m > 0.f) {
+      int e;
+      const float f = frexpf(m, &e);           // m / 2^sc <= 448 = 0.875 * 2^9
+      sc = min(max(f <= 0.875f ? e - 9 : e - 8, -127), 127);
+    }
+    const uint32_t code = e4m3_rne(ldexpf(r, -sc));
+    r -= ldexpf(e4m3_value(code), sc);
+    const int64_t pr = i * 4 + piece;
+    p.ql[pr * D + k] = (uint8_t)code;
+    if ((k & 31) == 0) p.ql_sf[pr * kNKB + (k >> 5)] = (uint8_t)(sc + 127);
+  }
+}
+
+template <int FMT, int D>
+static hipError_t launch_qsum_inst(const QsumParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((qsum_kernel<FMT, 64, D>), dim3((unsigned)p.sq), dim3(D), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_qsum(int fmt, int d, const QsumParams& p, hipStream_t s) {
+  if (p.sq == 0) return hipSuccess;
+  switch (fmt) {
+    case kFP8: return d == 64 ? launch_qsum_inst<kFP8, 64>(p, s) : launch_qsum_inst<kFP8, 128>(p, s);
+    case kMXFP8: return d == 64 ? launch_qsum_inst<kMXFP8, 64>(p, s) : launch_qsum_inst<kMXFP8, 128>(p, s);
+    default: return d == 64 ? launch_qsum_inst<kMXFP4, 64>(p, s) : launch_qsum_inst<kMXFP4, 128>(p, s);
+  }
+}
+
+}  // namespace mqa
