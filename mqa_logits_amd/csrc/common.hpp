@@ -123,12 +123,13 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
-// One operand from a buffer: 16 bytes at off_lo and 16 at off_hi (an offset
-// of kOOB reads as zero).
-__device__ __forceinline__ v8i buffer_operand(Rsrc r, int off_lo, int off_hi) {
+// One operand from a buffer: 16 bytes at off_lo + soff and 16 at off_hi +
+// soff (a lane offset of kOOB reads as zero).  soff is wave-uniform and rides
+// the instruction's scalar offset, which the range check includes.
+__device__ __forceinline__ v8i buffer_operand(Rsrc r, int off_lo, int off_hi, int soff = 0) {
   typedef int v4i __attribute__((ext_vector_type(4)));
-  const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, off_lo, 0, 0);
-  const v4i b = __builtin_amdgcn_raw_buffer_load_b128(r, off_hi, 0, 0);
+  const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, off_lo, soff, 0);
+  const v4i b = __builtin_amdgcn_raw_buffer_load_b128(r, off_hi, soff, 0);
   return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -240,13 +241,11 @@ struct RowGroup {
   static constexpr int kLag = kRing / 2;
   static constexpr int kValuPerTile = LIN ? 4 : 8;
   v4f acc[kRing];
-  v4f accl;                                    // LIN: the linear tile of the last step
   float s[4];
 
   __device__ __forceinline__ void start() {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
-    accl = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = 0.f;
   }
@@ -261,23 +260,28 @@ struct RowGroup {
     }
   }
 
-  // LIN: add the x / 2 half of the step whose linear tile is in accl.
-  __device__ __forceinline__ void add_lin() {
-    if constexpr (LIN) s[0] += (accl[0] + accl[1]) + (accl[2] + accl[3]);
-  }
 
-  __device__ __forceinline__ float take() {
+
+  // The finished step's total; the sums restart from the next step's linear
+  // tile (LIN, already issued) or from zero.
+  __device__ __forceinline__ float take(const v4f& next_lin) {
     const float v = (s[0] + s[1]) + (s[2] + s[3]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = 0.f;
+    for (int i = 0; i < 4; ++i) s[i] = LIN ? next_lin[i] : 0.f;
     return v;
   }
 
   // One step: issue its kMT MFMAs (operand b) while reducing the tiles kLag
   // behind; once the previous step's last tile is reduced (slot kLag - 1),
-  // done(total of the previous step) runs.
+  // done(total of the previous step) runs.  LIN: the linear tile goes first,
+  // and this step's sums start from it.
   template <class Done>
   __device__ __forceinline__ void step(const v8i& b, int scale_b, Done&& done) {
+    v4f lin = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (LIN) {
+      lin = mma_lin<FMT>(ql, b, qls, scale_b);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
 #pragma unroll
     for (int m = 0; m < kMT; ++m) {
       reduce_tile((m - kLag + kMT) % kMT, acc[(m - kLag + kRing) % kRing]);
@@ -287,14 +291,7 @@ struct RowGroup {
       acc[m % kRing] = c;
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerTile, 0);   // the reduction VALU
       __builtin_amdgcn_sched_group_barrier(0x008, kWays, 0);          // then the tile's MFMAs
-      if (m == kLag - 1) {
-        add_lin();
-        done(take());
-      }
-    }
-    if constexpr (LIN) {
-      accl = mma_lin<FMT>(ql, b, qls, scale_b);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m == kLag - 1) done(take(lin));
     }
   }
 
@@ -302,8 +299,7 @@ struct RowGroup {
   __device__ __forceinline__ float drain() {
 #pragma unroll
     for (int k = 0; k < kLag; ++k) reduce_tile(kMT - kLag + k, acc[(kMT - kLag + k) % kRing]);
-    add_lin();
-    return take();
+    return take(v4f{0.f, 0.f, 0.f, 0.f});
   }
 };
 

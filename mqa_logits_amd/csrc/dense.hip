@@ -151,14 +151,13 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   // operand, e8m0 scale (MX) and fp32 token scale (FP8) of step j0; tokens
   // past Skv read as zero.
   auto load_b = [&](int j0, KvOp& o) {
-    o.b = buffer_operand(kv_r, b_lo == kOOB ? kOOB : b_lo + j0 * kRowBytes,
-                         b_hi == kOOB ? kOOB : b_hi + j0 * kRowBytes);
+    o.b = buffer_operand(kv_r, b_lo, b_hi, j0 * kRowBytes);
     if constexpr (FmtInfo<FMT>::kMX) {
-      o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, sc_lane + j0 * kNKB, 0, 0) : 127;
+      o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, sc_lane, j0 * kNKB, 0) : 127;
       o.ks = 1.f;
     } else {
       o.bs = 127;
-      o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, sc_lane + 4 * j0, 0, 0));
+      o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, sc_lane, 4 * j0, 0));
     }
   };
 
@@ -169,15 +168,18 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   bool flip = false;
   if constexpr (!FmtInfo<FMT>::kMX) {
     if (cl < ch) {
-      // dword loads: each is wholly inside or outside the scale array
+      // 16-byte loads, 16 in flight per lane (4096 scales a round); the range
+      // check zero-fills dwords past the array, and scales of columns past
+      // the span only cost the exact path.
+      typedef int v4i __attribute__((ext_vector_type(4)));
       int neg = 0;
-      for (int j = cl + lane; j < ch; j += 16 * kWaveLanes) {
-        int s16[16];
+      for (int j = cl + 4 * lane; j < ch; j += 64 * kWaveLanes) {
+        v4i s16[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u)
-          s16[u] = __builtin_amdgcn_raw_buffer_load_b32(sc_r, 4 * (j + kWaveLanes * u), 0, 0);
+          s16[u] = __builtin_amdgcn_raw_buffer_load_b128(sc_r, 4 * (j + 4 * kWaveLanes * u), 0, 0);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) neg |= s16[u];
+        for (int u = 0; u < 16; ++u) neg |= (s16[u][0] | s16[u][1]) | (s16[u][2] | s16[u][3]);
       }
       flip = __ballot(neg < 0) != 0;           // any sign bit set (-0.0 is harmless)
     }
