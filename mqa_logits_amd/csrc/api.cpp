@@ -75,21 +75,17 @@ mqa_status check_common(mqa_dtype dt, const void* q, const uint8_t* q_sf, const 
   return MQA_OK;
 }
 
-// Columns per block: enough blocks to give every compute unit several, with
-// chunks of at least 256 tokens.  Any multiple of 16 is correct.
-int32_t pick_chunk(int32_t sq, int32_t skv) {
-  // Enough (row group, chunk) blocks to give every SIMD a few, with chunks a
-  // whole number of pipeline trips wide so only a row's last chunk is ragged.
-  constexpr int64_t kTargetBlocks = 2048;
-  constexpr int64_t kTrip = 16 * mqa::kKvStages;
-  const int64_t qblocks = (sq + 3) / 4;          // one wave (block) per 4 rows
+// Chunks per row group: about one wave per SIMD (a single dispatch round, one
+// prologue per SIMD; the chunks of a row group carry equal work), with runs
+// of at least 256 tokens.
+int32_t pick_chunks(int32_t sq, int32_t skv) {
+  constexpr int64_t kTargetBlocks = 1024 / mqa::kDenseWaves;
+  const int64_t qblocks = (sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves);
   int64_t n_chunks = (kTargetBlocks + qblocks - 1) / qblocks;
   const int64_t max_chunks = (skv + 255) / 256;
   if (n_chunks > max_chunks) n_chunks = max_chunks;
   if (n_chunks < 1) n_chunks = 1;
-  int64_t cols = (skv + n_chunks - 1) / n_chunks;
-  cols = (cols + kTrip - 1) / kTrip * kTrip;
-  return (int32_t)cols;
+  return (int32_t)n_chunks;
 }
 
 mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
@@ -114,13 +110,12 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   p.stride = stride;
   p.sq = sq;
   p.skv = skv;
-  p.chunk_cols = pick_chunk(sq, skv);
-  p.n_chunks = (skv + p.chunk_cols - 1) / p.chunk_cols;
-  const int64_t grid = (int64_t)((sq + 3) / 4) * p.n_chunks;
+  p.n_chunks = pick_chunks(sq, skv);
+  const int64_t grid = (int64_t)((sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves)) * p.n_chunks;
   if (grid > 0x7fffffff) return fail(MQA_ERR_UNSUPPORTED, "%s: problem too large", who);
   if (debug_enabled())
-    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d store=%d Sq=%d Skv=%d chunk=%d grid=%lld\n",
-            who, (int)dt, h, d, store, sq, skv, p.chunk_cols, (long long)grid);
+    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d store=%d Sq=%d Skv=%d chunks=%d grid=%lld\n",
+            who, (int)dt, h, d, store, sq, skv, p.n_chunks, (long long)grid);
   if (h != mqa::kLinHeads)
     return hip_status(mqa::launch_dense((int)dt, h, d, store, p, stream), who);
 

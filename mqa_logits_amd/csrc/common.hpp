@@ -311,7 +311,8 @@ struct KvOp {
   float ks;
 };
 
-// Walk the 16-token steps from cl of one wave.  The KV operands ride a ring
+// Walk the 16-token steps from cl of one wave (o[] prefetched by
+// prefetch_span).  The KV operands ride a ring
 // of kKvStages slots, slot k holding the steps k, k + kKvStages, ... of the
 // walk.  A step's total is known kLag tiles into the next step: it goes to
 // sink.put(u, j0, v), u = the position of step j0 in its trip of kKvStages
@@ -326,14 +327,20 @@ struct KvOp {
 // sinks drop columns below cl.  load(j0, KvOp&) must zero-fill tokens past
 // the KV range and the sink must drop columns past the caller's range.
 // Returns the first column not walked.
+// The ring's first kKvStages - 1 steps of a walk from cl (issued early, so
+// their latency overlaps whatever the caller still has to settle).
+template <class Load>
+__device__ __forceinline__ void prefetch_span(int cl, KvOp (&o)[kKvStages], Load&& load) {
+#pragma unroll
+  for (int u = 0; u < kKvStages - 1; ++u) load(cl + u * kTileN, o[u]);
+}
+
 template <bool FLIP, class RG, class Load, class Sink>
-__device__ __forceinline__ int compute_span(RG& rg, int cl, int ch, Load&& load, Sink& sink) {
+__device__ __forceinline__ int compute_span(RG& rg, int cl, int ch, KvOp (&o)[kKvStages],
+                                            Load&& load, Sink& sink) {
   constexpr int S = kKvStages;
   const int steps = (ch - cl + kTileN - 1) / kTileN;
   const int end = cl + (steps + S - 1) / S * S * kTileN;
-  KvOp o[S];
-#pragma unroll
-  for (int u = 0; u < S - 1; ++u) load(cl + u * kTileN, o[u]);
   o[S - 1].ks = 0.f;                           // the phantom step cl - 16
   rg.start();
 

@@ -9,9 +9,10 @@
 // Architecture Components) and "[PR #435] Improve SM100 MX MQA logits
 // clean-output performance" (Description).
 //
-// Work split: a block is one wave; it owns 4 consecutive query rows and one
-// chunk of KV columns, keeps the rows' Q operands and weights in registers
-// and walks the chunk 16 tokens at a time.  Tokens outside the
+// Work split: a wave owns 4 consecutive query rows and one chunk of KV
+// columns, keeps the rows' Q operands and weights in registers and walks the
+// chunk 16 tokens at a time; the 4 waves of a block take 4 consecutive row
+// groups and the same chunk.  Tokens outside the
 // union of its rows' ranges are -inf fill (no MFMA); tokens inside are
 // computed and masked per row in the same store.  No second pass, no atomics:
 // each output element is written by exactly one lane.
@@ -58,23 +59,28 @@ struct StagedSink {
   __device__ __forceinline__ void finish() { buffer_store4_nt(r, pend_off, pend); }
 };
 
+constexpr int kDenseThreads = kWaveLanes * kDenseWaves;
+
 template <int FMT, int H, int D, int STORE>
-__global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) {
   using RG = RowGroup<FMT, H, D, H == kLinHeads>;
   using L = OperandLayout<FMT, D>;
   constexpr int kNKB = RG::kNKB;
   constexpr int kRowBytes = RG::kRowBytes;
 
   const int lane = threadIdx.x & (kWaveLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Blocks (one wave each) are dispatched round-robin over the 8 XCDs;
-  // renumber them so each XCD gets a contiguous run of (row group, chunk)
-  // work and its L2 keeps that run's Q rows.
+  // Blocks are dispatched round-robin over the 8 XCDs; renumber them so each
+  // XCD gets a contiguous run of (row-group block, chunk) work and its L2
+  // keeps that run's Q rows.  Wave w of a block takes row group
+  // kDenseWaves * (block's row-group index) + w.
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int rgroup = bid / p.n_chunks;
-  const int chunk = bid - rgroup * p.n_chunks;
+  const int rblock = bid / p.n_chunks;
+  const int chunk = bid - rblock * p.n_chunks;
+  const int rgroup = rblock * kDenseWaves + wave;
 
   const int row0 = rgroup * kRowsPerWave;
   if (row0 >= p.sq) return;
@@ -87,31 +93,51 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   const int e_row_c = min(e_row, p.sq - 1);
   const int a_row_c = min(row0 + ((lane >> 2) & 3), p.sq - 1);
 
+  // The 4 rows' ranges (wave-uniform loads) go out first: the column split
+  // needs them, and in-order load completion would otherwise make them wait
+  // for the Q operands, the largest loads of the prologue.
+  int ks_raw[kRowsPerWave], ke_raw[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int rr = min(row0 + r, p.sq - 1);
+    ks_raw[r] = p.k_start[rr];
+    ke_raw[r] = p.k_end[rr];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   RG rg;
   rg.load(p.q, p.q_sf, p.w, a_row_c, e_row_c, lane);
   rg.load_lin(p.ql, p.ql_sf, a_row_c, lane);
+  __builtin_amdgcn_sched_barrier(0);
 
-  const int s_row = clampi(p.k_start[e_row_c], 0, p.skv);
-  int e_end = clampi(p.k_end[e_row_c], s_row, p.skv);
-  if (!row_ok) e_end = s_row;
-
-  // Union of the 4 rows' ranges (wave-uniform).
+  // The ranges, their union, and this lane's row.
+  int s_r[kRowsPerWave], e_r[kRowsPerWave];
   int lo = 0x7fffffff, hi = 0;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int s_r = __builtin_amdgcn_readlane(s_row, 16 * r);
-    const int e_r = __builtin_amdgcn_readlane(e_end, 16 * r);
-    if (e_r > s_r) {
-      lo = min(lo, s_r);
-      hi = max(hi, e_r);
+    s_r[r] = clampi(ks_raw[r], 0, p.skv);
+    e_r[r] = row0 + r < p.sq ? clampi(ke_raw[r], s_r[r], p.skv) : s_r[r];
+    if (e_r[r] > s_r[r]) {
+      lo = min(lo, s_r[r]);
+      hi = max(hi, e_r[r]);
     }
   }
+  const int s_row = g == 0 ? s_r[0] : g == 1 ? s_r[1] : g == 2 ? s_r[2] : s_r[3];
+  const int e_end = g == 0 ? e_r[0] : g == 1 ? e_r[1] : g == 2 ? e_r[2] : e_r[3];
 
-  // Chunks are whole trips wide, so c0 and cl below are trip-aligned.
-  const int c0 = chunk * p.chunk_cols;
-  const int c1 = min(c0 + p.chunk_cols, p.skv);
-  int cl = max(c0, lo & ~(kTripCols - 1));
-  int ch = min(c1, hi);
+  // The union, from a trip-aligned start, splits into n_chunks runs of whole
+  // trips of nearly equal length; block `chunk` computes its run [cl, ch) and
+  // owns the output columns [c0, c1) around it (from column 0 for the first
+  // chunk, up to Skv for the last), so the blocks of a row group partition
+  // the row and do the same amount of MFMA work.
+  const bool any = lo < hi;
+  const int lo64 = any ? (lo & ~(kTripCols - 1)) : 0;
+  const int trips = any ? (hi - lo64 + kTripCols - 1) / kTripCols : 0;
+  const int b0 = min(lo64 + (int)((int64_t)chunk * trips / p.n_chunks) * kTripCols, p.skv);
+  const int b1 = min(lo64 + (int)((int64_t)(chunk + 1) * trips / p.n_chunks) * kTripCols, p.skv);
+  const int c0 = chunk == 0 ? 0 : b0;
+  const int c1 = chunk == p.n_chunks - 1 ? p.skv : b1;
+  int cl = b0, ch = min(b1, hi);
   if (cl >= ch) { cl = c1; ch = c1; }          // nothing to compute in this chunk
   const int len = max(0, min(e_end, c1) - s_row);
   const int rel_n = n - s_row;                 // (j0 + rel_n) in [0, len) iff in range
@@ -161,6 +187,11 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
     }
   };
 
+  // The walk's first operands go out before the scale scan below, so both
+  // latencies overlap (and that of the Q loads above).
+  KvOp ring[kKvStages];
+  if (cl < ch) prefetch_span(cl, ring, load_b);
+
   // For FP8 a negative token scale is applied exactly by negating that
   // token's codes: ReLU(s * x) = |s| * ReLU(sign(s) * x).  Whether any scale
   // of the span is negative is settled once, before the loop, so the hot
@@ -168,18 +199,19 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   bool flip = false;
   if constexpr (!FmtInfo<FMT>::kMX) {
     if (cl < ch) {
-      // 16-byte loads, 16 in flight per lane (4096 scales a round); the range
+      // 16-byte loads, 32 in flight per lane (8192 scales a round); the range
       // check zero-fills dwords past the array, and scales of columns past
       // the span only cost the exact path.
       typedef int v4i __attribute__((ext_vector_type(4)));
+      constexpr int kPer = 32;
       int neg = 0;
-      for (int j = cl + 4 * lane; j < ch; j += 64 * kWaveLanes) {
-        v4i s16[16];
+      for (int j = cl + 4 * lane; j < ch; j += 4 * kPer * kWaveLanes) {
+        v4i sv[kPer];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          s16[u] = __builtin_amdgcn_raw_buffer_load_b128(sc_r, 4 * (j + 4 * kWaveLanes * u), 0, 0);
+        for (int u = 0; u < kPer; ++u)
+          sv[u] = __builtin_amdgcn_raw_buffer_load_b128(sc_r, 4 * (j + 4 * kWaveLanes * u), 0, 0);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) neg |= (s16[u][0] | s16[u][1]) | (s16[u][2] | s16[u][3]);
+        for (int u = 0; u < kPer; ++u) neg |= (sv[u][0] | sv[u][1]) | (sv[u][2] | sv[u][3]);
       }
       flip = __ballot(neg < 0) != 0;           // any sign bit set (-0.0 is harmless)
     }
@@ -188,14 +220,15 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
   auto walk = [&](auto& sink) {
     int walked = ch;
     if (cl < ch) {
-      if (flip) walked = compute_span<true>(rg, cl, ch, load_b, sink);
-      else walked = compute_span<false>(rg, cl, ch, load_b, sink);
+      if (flip) walked = compute_span<true>(rg, cl, ch, ring, load_b, sink);
+      else walked = compute_span<false>(rg, cl, ch, ring, load_b, sink);
     }
     return walked;
   };
 
   if constexpr (STORE == kDenseClean) {
-    __shared__ __attribute__((aligned(16))) float stage[2 * kRowsPerWave * kTripCols];
+    __shared__ __attribute__((aligned(16))) float stage_all[kDenseWaves][2 * kRowsPerWave * kTripCols];
+    float* stage = stage_all[wave];
     const int rows = min(kRowsPerWave, p.sq - row0);
     const int col4 = 4 * n;                     // lane l's group: row g, columns col4 .. col4 + 3
     const bool grp_ok = g < rows;
@@ -237,9 +270,9 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(DenseParams p) {
 
 template <int FMT, int H, int D, int STORE>
 static hipError_t launch_dense_inst(const DenseParams& p, hipStream_t stream) {
-  const int rgroups = (p.sq + kRowsPerWave - 1) / kRowsPerWave;
-  const int64_t grid = (int64_t)rgroups * p.n_chunks;
-  hipLaunchKernelGGL((dense_kernel<FMT, H, D, STORE>), dim3((unsigned)grid), dim3(kThreads), 0,
+  const int rblocks = (p.sq + kRowsPerWave * kDenseWaves - 1) / (kRowsPerWave * kDenseWaves);
+  const int64_t grid = (int64_t)rblocks * p.n_chunks;
+  hipLaunchKernelGGL((dense_kernel<FMT, H, D, STORE>), dim3((unsigned)grid), dim3(kDenseThreads), 0,
                      stream, p);
   return hipGetLastError();
 }

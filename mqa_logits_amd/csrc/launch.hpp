@@ -9,10 +9,14 @@ namespace mqa {
 // Output modes of the dense kernel.
 enum Store : int { kDenseClean = 0, kDenseKeep = 1, kCompressed = 2 };
 
-// Waves per block of the dense and paged kernels.  One: every value a wave
-// needs to be uniform (its rows, its chunk, its buffer resources) then comes
-// from blockIdx and the kernel arguments, which live in SGPRs already.
+// Waves per block of the paged kernel.  One: every value a wave needs to be
+// uniform (its schedule slot, its buffer resources) then comes from blockIdx
+// and the kernel arguments, which live in SGPRs already.
 constexpr int kWavesPerBlock = 1;
+// Waves per block of the dense kernel: one per SIMD of a compute unit, each
+// on its own 4-row group, all walking the same chunk of KV columns, so a KV
+// tile comes from L2 once per CU and from the CU's L1 for the other waves.
+constexpr int kDenseWaves = 4;
 // Resident waves per compute unit the kernels are sized for (one per SIMD).
 constexpr int kWavesPerCu = 4;
 // KV operand buffers in flight per wave: a step's operands are requested
@@ -33,8 +37,7 @@ struct DenseParams {
   float* out;
   int64_t stride;          // dense row stride in elements
   int32_t sq, skv;
-  int32_t chunk_cols;      // KV columns per block, a multiple of 16 * kKvStages
-  int32_t n_chunks;        // ceil(Skv / chunk_cols)
+  int32_t n_chunks;        // chunks per 4-row group (each computes an equal run of the rows' range)
   const uint8_t* ql;       // [Sq, 4, D] e4m3 pieces of the weighted query sum (H = 64)
   const uint8_t* ql_sf;    // [Sq, 4, D/32] their e8m0 scales
 };

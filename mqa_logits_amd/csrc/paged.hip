@@ -113,7 +113,9 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
       // Paged decode is bound by the KV gather, so FP8 always takes the
       // sign-exact path (negative token scales negate the token's codes)
       // instead of scanning the scales first.
-      compute_span<!FmtInfo<FMT>::kMX>(rg, col0, col1, load, sink);
+      KvOp o[kKvStages];
+      prefetch_span(col0, o, load);
+      compute_span<!FmtInfo<FMT>::kMX>(rg, col0, col1, o, load, sink);
     }
     blk = seg_end;
   }
