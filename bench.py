@@ -36,6 +36,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_digest():
+    """sha256 over the HIP sources, so traffic counted for older kernels is not reused."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mqa_logits_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (profiles/<kernel>_<workload>_traffic.txt), if it was taken
+    on the current kernel sources; None otherwise."""
+    import glob
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_traffic.txt")))
+    if not paths:
+        return None
+    path = paths[0]
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def clamped_ranges(k_start, k_end, skv):
     """Row ranges as the metric counts them: [clamp(s,0,Skv), clamp(e,s,Skv))."""
     s = np.clip(np.asarray(k_start, np.int64), 0, skv)
@@ -180,8 +214,10 @@ def cpu_baseline(info, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU raises its clocks only after tens of milliseconds of sustained
+    # load; the default warmup (~40 ms at the default workload) lets it settle.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -210,19 +246,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-launch HIP events on the launch stream
+    # timed region: K back-to-back steps between two HIP events on the launch
+    # stream (an event per step would put a cache-flushing marker between the
+    # launches and time that too)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(args.steps):
         step()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    per_launch_ms = a.elapsed_time(b) / args.steps
 
     flops = info["flops"]
     value = flops * args.steps / wall / 1e12
@@ -230,11 +268,11 @@ def main():
         achieved = flops / (per_launch_ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS[info["fmt"]]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None}
+                "frac": achieved / peak, "traffic": measured_traffic(args.workload)}
     else:
         achieved = info["bytes"] / (per_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(info, args.cpu_seconds)
     line = {
