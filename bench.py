@@ -36,12 +36,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest():
-    """sha256 over the HIP sources, so traffic counted for older kernels is not reused."""
+def kernel_source_digest(names):
+    """sha256 over the named files of mqa_logits_amd/csrc, so traffic counted
+    for older kernels is not reused."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mqa_logits_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -62,12 +63,81 @@ def measured_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != kernel_source_digest():
+    names = fields.get("sources", "").split()
+    try:
+        if not names or fields.get("source_sha256") != kernel_source_digest(names):
+            return None
+    except OSError:
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+class SclkSampler:
+    """Samples the current shader clock from sysfs (pp_dpm_sclk, the line
+    marked '*') in a background thread; mean() is None where unreadable."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.samples = []
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower()
+                                     .replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def mean(self):
+        return float(np.mean(self.samples)) if self.samples else None
+
+
+def mfma_microbench():
+    """Dense fp8 MFMA rate and shader clock from libmqa_peak.so (one wave per
+    SIMD, chains of the same MFMA the kernels use); None if unavailable."""
+    import ctypes
+    import mqa_logits_amd as mq
+    path = os.path.join(os.path.dirname(mq.LIB_PATH), "libmqa_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.mqa_measure_mfma_peak
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                   ctypes.POINTER(ctypes.c_double)]
+    fn.restype = ctypes.c_int
+    t, c = ctypes.c_double(), ctypes.c_double()
+    if fn(mq.mqa_num_cus(0) * 4, 4000, ctypes.byref(t), ctypes.byref(c)) != 0:
+        return None
+    return {"tflops": t.value, "sclk_mhz": c.value}
 
 
 def clamped_ranges(k_start, k_end, skv):
@@ -121,6 +191,7 @@ def build_step(name):
             mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o)
         nvalid = valid_entries_dense(case)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
+                    out_bytes=4.0 * case.sq * case.skv,
                     sq=case.sq, skv=case.skv, h=case.h, d=case.d, outs=outs,
                     cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
                              format=case.fmt, layout="dense", clean_logits=True))
@@ -146,6 +217,7 @@ def build_step(name):
                                      row_offsets=off, out=o)
         nvalid = valid_entries_dense(case)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
+                    out_bytes=4.0 * total,
                     cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
                              format=case.fmt, layout="compressed"))
         return step, info
@@ -179,6 +251,7 @@ def build_step(name):
     kv_bytes = n_units * case.block_size * (row_bytes + 4)
     out_bytes = rows * case.max_context_len * 4
     info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="hbm",
+                out_bytes=out_bytes,
                 bytes=kv_bytes + out_bytes + case.q.nbytes + case.weights.nbytes,
                 cfg=dict(batch=case.batch, next_n=case.next_n, heads=case.h, head_dim=case.d,
                          block_size=case.block_size, max_context_len=case.max_context_len,
@@ -254,11 +327,12 @@ def main():
     b = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    a.record(stream)
-    for _ in range(args.steps):
-        step()
-    b.record(stream)
-    torch.cuda.synchronize()
+    with SclkSampler() as sclk:
+        a.record(stream)
+        for _ in range(args.steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_launch_ms = a.elapsed_time(b) / args.steps
 
@@ -274,6 +348,7 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
 
+    peak_probe = mfma_microbench()
     cpu = None if args.no_cpu_baseline else cpu_baseline(info, args.cpu_seconds)
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -285,6 +360,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_ms": per_launch_ms,
+        "sclk_mhz_during_timing": sclk.mean(),
+        "mfma_microbench": peak_probe,
+        "hbm_write_gbs": info["out_bytes"] / (per_launch_ms * 1e-3) / 1e9,
     }
     print(json.dumps(line), flush=True)
 

@@ -21,6 +21,9 @@ LIB = os.path.join(PKG, "libmqa_logits.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["dense.hip", "qsum.hip", "paged.hip", "api.cpp"]
+# measurement aid for bench.py, linked into a library of its own
+PROBE_SOURCES = ["peak.hip"]
+PROBE_LIB = os.path.join(PKG, "libmqa_peak.so")
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 COMMON_FLAGS = [
@@ -58,8 +61,15 @@ def build(verbose=True):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB)
+    pobjs = [_compile(src) for src in PROBE_SOURCES]
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *pobjs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
