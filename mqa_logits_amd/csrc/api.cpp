@@ -8,7 +8,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "launch.hpp"
 
@@ -88,6 +91,55 @@ int32_t pick_chunks(int32_t sq, int32_t skv) {
   return (int32_t)n_chunks;
 }
 
+// Workspace of the weighted query sum, one per (device, stream): work on a
+// stream runs in order, so consecutive calls on it can share one buffer, and
+// a steady sequence of calls allocates nothing.  It grows when a call needs
+// more (hipFree of the old one waits for the work using it) and lives until
+// the process ends.
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+
+hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  auto& slot = g_ws[{dev, stream}];
+  if (slot.second < bytes) {
+    if (slot.first) {
+      e = hipFree(slot.first);
+      slot = {nullptr, 0};
+      if (e != hipSuccess) return e;
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    slot = {p, bytes};
+  }
+  *out = slot.first;
+  return hipSuccess;
+}
+
+// H = 64: the kernels take the linear half of ReLU from the weighted query
+// sum's pieces (qsum.hip), written into the stream's workspace right before
+// the launch that reads them.
+template <class Launch>
+mqa_status with_qsum(mqa_dtype dt, const void* q, const uint8_t* q_sf, const float* weights,
+                     int32_t rows, int32_t d, const uint8_t** ql, const uint8_t** ql_sf,
+                     hipStream_t stream, const char* who, Launch&& launch) {
+  const size_t ql_bytes = (size_t)rows * 4 * d, sf_bytes = (size_t)rows * 4 * (d / 32);
+  void* ws = nullptr;
+  hipError_t e = workspace(stream, ql_bytes + sf_bytes + 16, &ws);
+  if (e != hipSuccess) return hip_status(e, who);
+  mqa::QsumParams qp{static_cast<const uint8_t*>(q), q_sf, weights, static_cast<uint8_t*>(ws),
+                     static_cast<uint8_t*>(ws) + ql_bytes, rows};
+  *ql = qp.ql;
+  *ql_sf = qp.ql_sf;
+  e = mqa::launch_qsum((int)dt, d, qp, stream);
+  if (e == hipSuccess) e = launch();
+  return hip_status(e, who);
+}
+
 mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
                      const uint8_t* kv_sf, const float* kv_scale, const float* weights,
                      const int32_t* k_start, const int32_t* k_end, const int64_t* row_off,
@@ -118,21 +170,8 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
             who, (int)dt, h, d, store, sq, skv, p.n_chunks, (long long)grid);
   if (h != mqa::kLinHeads)
     return hip_status(mqa::launch_dense((int)dt, h, d, store, p, stream), who);
-
-  // H = 64: the weighted query sum's pieces live in a stream-ordered
-  // workspace for the duration of the call.
-  const size_t ql_bytes = (size_t)sq * 4 * d, sf_bytes = (size_t)sq * 4 * (d / 32);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, ql_bytes + sf_bytes + 16, stream);
-  if (e != hipSuccess) return hip_status(e, who);
-  mqa::QsumParams qp{p.q, q_sf, weights, static_cast<uint8_t*>(ws),
-                     static_cast<uint8_t*>(ws) + ql_bytes, sq};
-  p.ql = qp.ql;
-  p.ql_sf = qp.ql_sf;
-  e = mqa::launch_qsum((int)dt, d, qp, stream);
-  if (e == hipSuccess) e = mqa::launch_dense((int)dt, h, d, store, p, stream);
-  const hipError_t ef = hipFreeAsync(ws, stream);
-  return hip_status(e != hipSuccess ? e : ef, who);
+  return with_qsum(dt, q, q_sf, weights, sq, d, &p.ql, &p.ql_sf, stream, who,
+                   [&] { return mqa::launch_dense((int)dt, h, d, store, p, stream); });
 }
 
 }  // namespace

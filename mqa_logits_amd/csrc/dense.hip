@@ -21,44 +21,6 @@
 
 namespace mqa {
 
-constexpr int kTripCols = kTileN * kKvStages;  // columns per pipeline trip
-
-// Clean dense output.  A trip's 4 rows x kTripCols columns are staged in LDS
-// and leave as one 16-byte store per lane (lane l: row l / 16, columns
-// 4 (l % 16) .. +3 of the trip), so every row gets whole 256-byte runs
-// instead of a 64-byte piece per step: HBM never has to fetch an output line
-// to merge a partial write.  Trips alternate between two LDS buffers; a
-// trip's group is read back right after its last put and stored one step
-// later, when the read has long returned.
-struct StagedSink {
-  float* stage;              // 2 x [4][kTripCols] floats in LDS
-  Rsrc r;
-  int base;                  // first column of the walk (trip-aligned)
-  int put_idx;               // this lane's slot: row g, column n of a trip's first step
-  int rd_idx;                // this lane's group: row l / 16, column 4 (l % 16)
-  int row_off;               // byte offset of this lane's group in the output, column 0
-  int last_j0;               // the group of trip j0 is stored iff base <= j0 <= last_j0
-  int rel_n, len;            // column j0 + n is in range iff j0 + rel_n in [0, len)
-  float4 pend;               // the last trip read back, and its store offset
-  int pend_off;
-
-  __device__ __forceinline__ float* buffer(int j0) const {
-    return stage + (((j0 - base) >> 6) & 1) * (kRowsPerWave * kTripCols);
-  }
-  __device__ __forceinline__ void put(int u, int j0, float v) {
-    const bool in_range = (uint32_t)(j0 + rel_n) < (uint32_t)len;
-    buffer(j0)[put_idx + u * kTileN] = in_range ? v : neg_inf();
-    if (u == 0) buffer_store4_nt(r, pend_off, pend);
-  }
-  __device__ __forceinline__ void trip(int jt) {
-    asm volatile("" ::: "memory");            // the group read follows every lane's writes
-    pend = *reinterpret_cast<const float4*>(buffer(jt) + rd_idx);
-    pend_off = (jt >= base && jt <= last_j0) ? row_off + 4 * jt : kOOB;
-    asm volatile("" ::: "memory");
-  }
-  __device__ __forceinline__ void finish() { buffer_store4_nt(r, pend_off, pend); }
-};
-
 constexpr int kDenseThreads = kWaveLanes * kDenseWaves;
 
 template <int FMT, int H, int D, int STORE>

@@ -20,6 +20,8 @@ namespace mqa {
 
 template <int FMT, int H, int D, bool CLEAN>
 __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
+  // Decode batches are small: the weighted-query-sum launch would cost more
+  // than the halved epilogue saves, so the paged kernel keeps max + fma.
   using RG = RowGroup<FMT, H, D>;
   using L = OperandLayout<FMT, D>;
   constexpr int kNKB = RG::kNKB;
@@ -56,6 +58,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
   const int eb = p.sched[2 * worker + 2];
   const int eblk = p.sched[2 * worker + 3];
 
+  __shared__ __attribute__((aligned(16))) float stage[2 * kRowsPerWave * kTripCols];
+  const float4 ninf4 = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
   RG rg;
   while (b < p.batch && (b < eb || (b == eb && blk < eblk))) {
     const int ctx = p.ctx[b];
@@ -99,23 +103,36 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
           o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, (tok + n) * 4, 0, 0));
         }
       };
-      auto off = [&](int j0, float& v) {
-        const bool in_range = j0 + rel_n < 0;
-        if constexpr (CLEAN) {
-          v = in_range ? v : neg_inf();
-          return j0 < wlim_n ? lane_off + 4 * j0 : kOOB;
-        } else {
-          return (j0 < wlim_n && in_range) ? lane_off + 4 * j0 : kOOB;
-        }
-      };
-      DwordSink<decltype(off)> sink{out_r, off, col0};
-
       // Paged decode is bound by the KV gather, so FP8 always takes the
       // sign-exact path (negative token scales negate the token's codes)
       // instead of scanning the scales first.
+      constexpr bool kFlip = !FmtInfo<FMT>::kMX;
       KvOp o[kKvStages];
       prefetch_span(col0, o, load);
-      compute_span<!FmtInfo<FMT>::kMX>(rg, col0, col1, o, load, sink);
+      if constexpr (CLEAN) {
+        // Whole 16-byte groups of the window through LDS (lane l: row l / 16,
+        // columns 4 (l % 16) .. +3 of a trip); in range iff column < e_tok.
+        const int lim = col1 & ~3;
+        const int last_j0 = row_ok ? lim - 4 * n - 4 : -0x40000000;
+        StagedSink sink{stage, out_r, col0, g * kTripCols + n, g * kTripCols + 4 * n,
+                        (t_e * (int)p.stride + 4 * n) * 4, last_j0, n, e_tok, ninf4, kOOB};
+        const int walked = compute_span<kFlip>(rg, col0, col1, o, load, sink);
+        if ((col1 & 3) != 0) {             // max_ctx not a multiple of 4: 1..3 columns
+          const int gs = col1 & ~3, jt = walked - kTripCols;
+          if (row_ok && gs + n < col1) {
+            float v = neg_inf();
+            if (gs >= jt && gs < walked) v = sink.buffer(jt)[g * kTripCols + (gs - jt) + n];
+            buffer_store_nt(out_r, (t_e * (int)p.stride + gs + n) * 4, v);
+          }
+        }
+      } else {
+        auto off = [&](int j0, float& v) {
+          (void)v;
+          return (j0 < wlim_n && j0 + rel_n < 0) ? lane_off + 4 * j0 : kOOB;
+        };
+        DwordSink<decltype(off)> sink{out_r, off, col0};
+        compute_span<kFlip>(rg, col0, col1, o, load, sink);
+      }
     }
     blk = seg_end;
   }
@@ -130,10 +147,14 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
       if (c < ((len + bs - 1) >> bs_shift)) continue;
       const Rsrc out_r = make_rsrc(p.out + (int64_t)fb * p.next_n * p.stride,
                                    (uint32_t)(p.next_n * p.stride * 4));
-      const int lane_off = (t_e * (int)p.stride + n) * 4;
+      // 16-byte groups (lane l: row l / 16, columns 4 (l % 16) .. +3), then
+      // the 1..3 columns of a last group cut by max_ctx
+      const int grp_off = (t_e * (int)p.stride + 4 * n) * 4;
       const int c1 = min((c + 1) << bs_shift, p.max_ctx);
-      for (int j0 = c << bs_shift; j0 < c1; j0 += kTileN)
-        buffer_store_nt(out_r, (row_ok && j0 + n < c1) ? lane_off + 4 * j0 : kOOB, neg_inf());
+      for (int j0 = c << bs_shift; j0 < c1; j0 += kTripCols)
+        buffer_store4_nt(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + 4 * j0 : kOOB, ninf4);
+      if ((c1 & 3) != 0 && row_ok && (c1 & ~3) + n < c1 && (c1 & ~3) >= (c << bs_shift))
+        buffer_store_nt(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * 4, neg_inf());
     }
   }
 }

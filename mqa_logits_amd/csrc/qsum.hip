@@ -55,18 +55,29 @@ __global__ __launch_bounds__(D) void qsum_kernel(QsumParams p) {
   const int64_t i = blockIdx.x;
   const int k = threadIdx.x;
 
-  float acc = 0.f;
+  // All H codes, scales and weights of the row are requested before any is
+  // used (one memory round trip, not H).
+  uint32_t code[H];
+  uint32_t sf[FmtInfo<FMT>::kMX ? H : 1];
+  float wt[H];
+#pragma unroll
   for (int h = 0; h < H; ++h) {
     const int64_t hr = i * H + h;
+    code[h] = p.q[hr * kRowBytes + (FMT == kMXFP4 ? (k >> 1) : k)];
+    if constexpr (FmtInfo<FMT>::kMX) sf[h] = p.q_sf[hr * kNKB + (k >> 5)];
+    wt[h] = p.w[hr];
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
     float v;
     if constexpr (FMT == kMXFP4) {
-      const uint32_t b = p.q[hr * kRowBytes + (k >> 1)];
-      v = e2m1_value((k & 1) ? b >> 4 : b & 15u);
+      v = e2m1_value((k & 1) ? code[h] >> 4 : code[h] & 15u);
     } else {
-      v = e4m3_value(p.q[hr * kRowBytes + k]);
+      v = e4m3_value(code[h]);
     }
-    if constexpr (FmtInfo<FMT>::kMX) v = ldexpf(v, (int)p.q_sf[hr * kNKB + (k >> 5)] - 127);
-    acc = __builtin_fmaf(0.5f * p.w[hr], v, acc);
+    if constexpr (FmtInfo<FMT>::kMX) v = ldexpf(v, (int)sf[h] - 127);
+    acc = __builtin_fmaf(0.5f * wt[h], v, acc);
   }
 
   // Four pieces: each takes the block's residual at the largest e8m0 scale
