@@ -48,63 +48,86 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
   return s | ((uint32_t)be << 3) | m;
 }
 
+// Thread t of a row handles elements 4t .. 4t+3 (one dword of fp8 codes, two
+// bytes of fp4 codes per head); 8 consecutive threads cover one 32-element
+// scale block.  kRowsPerBlock rows per block of 256 threads.
+template <int D>
+struct QsumShape {
+  static constexpr int kThreadsPerRow = D / 4;
+  static constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+};
+
 template <int FMT, int H, int D>
-__global__ __launch_bounds__(D) void qsum_kernel(QsumParams p) {
+__global__ __launch_bounds__(256) void qsum_kernel(QsumParams p) {
+  using S = QsumShape<D>;
   constexpr int kRowBytes = FMT == kMXFP4 ? D / 2 : D;
   constexpr int kNKB = D / 32;
-  const int64_t i = blockIdx.x;
-  const int k = threadIdx.x;
+  const int t = threadIdx.x % S::kThreadsPerRow;
+  const int64_t i = (int64_t)blockIdx.x * S::kRowsPerBlock + threadIdx.x / S::kThreadsPerRow;
+  if (i >= p.sq) return;                       // whole rows (and scale blocks) leave together
+  const int k0 = 4 * t;
 
-  // All H codes, scales and weights of the row are requested before any is
-  // used (one memory round trip, not H).
+  // All H code words, scales and weights of the row are requested before any
+  // is used (one memory round trip, not H).
   uint32_t code[H];
   uint32_t sf[FmtInfo<FMT>::kMX ? H : 1];
   float wt[H];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const int64_t hr = i * H + h;
-    code[h] = p.q[hr * kRowBytes + (FMT == kMXFP4 ? (k >> 1) : k)];
-    if constexpr (FmtInfo<FMT>::kMX) sf[h] = p.q_sf[hr * kNKB + (k >> 5)];
+    if constexpr (FMT == kMXFP4) {
+      code[h] = *reinterpret_cast<const uint16_t*>(p.q + hr * kRowBytes + (k0 >> 1));
+    } else {
+      code[h] = *reinterpret_cast<const uint32_t*>(p.q + hr * kRowBytes + k0);
+    }
+    if constexpr (FmtInfo<FMT>::kMX) sf[h] = p.q_sf[hr * kNKB + (k0 >> 5)];
     wt[h] = p.w[hr];
   }
-  float acc = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    float v;
-    if constexpr (FMT == kMXFP4) {
-      v = e2m1_value((k & 1) ? code[h] >> 4 : code[h] & 15u);
-    } else {
-      v = e4m3_value(code[h]);
+    const float wh = 0.5f * wt[h];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = FMT == kMXFP4 ? e2m1_value((code[h] >> (4 * e)) & 15u)
+                              : e4m3_value((code[h] >> (8 * e)) & 255u);
+      if constexpr (FmtInfo<FMT>::kMX) v = ldexpf(v, (int)sf[h] - 127);
+      acc[e] = __builtin_fmaf(wh, v, acc[e]);
     }
-    if constexpr (FmtInfo<FMT>::kMX) v = ldexpf(v, (int)sf[h] - 127);
-    acc = __builtin_fmaf(0.5f * wt[h], v, acc);
   }
 
   // Four pieces: each takes the block's residual at the largest e8m0 scale
   // that keeps every element within e4m3's range.
-  float r = acc;
+  float r[4] = {acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
   for (int piece = 0; piece < 4; ++piece) {
-    float m = fabsf(r);
+    float m = fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3])));
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));   // the 32-element block
+    for (int o = 4; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));   // the 8 threads of a block
     int sc = -127;
     if (m > 0.f) {
       int e;
       const float f = frexpf(m, &e);           // m / 2^sc <= 448 = 0.875 * 2^9
       sc = min(max(f <= 0.875f ? e - 9 : e - 8, -127), 127);
     }
-    const uint32_t code = e4m3_rne(ldexpf(r, -sc));
-    r -= ldexpf(e4m3_value(code), sc);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t c = e4m3_rne(ldexpf(r[e], -sc));
+      r[e] -= ldexpf(e4m3_value(c), sc);
+      word |= c << (8 * e);
+    }
     const int64_t pr = i * 4 + piece;
-    p.ql[pr * D + k] = (uint8_t)code;
-    if ((k & 31) == 0) p.ql_sf[pr * kNKB + (k >> 5)] = (uint8_t)(sc + 127);
+    *reinterpret_cast<uint32_t*>(p.ql + pr * D + k0) = word;
+    if ((t & 7) == 0) p.ql_sf[pr * kNKB + (k0 >> 5)] = (uint8_t)(sc + 127);
   }
 }
 
 template <int FMT, int D>
 static hipError_t launch_qsum_inst(const QsumParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((qsum_kernel<FMT, 64, D>), dim3((unsigned)p.sq), dim3(D), 0, s, p);
+  using S = QsumShape<D>;
+  const int blocks = (p.sq + S::kRowsPerBlock - 1) / S::kRowsPerBlock;
+  hipLaunchKernelGGL((qsum_kernel<FMT, 64, D>), dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
