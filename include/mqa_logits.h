@@ -128,7 +128,7 @@ mqa_status mqa_logits_compressed(mqa_dtype dt,
  * floor((c+1)*W/num_splits)).  schedule [num_splits + 1][2] int32 receives
  * (b, blk) of the first unit of each piece, and (batch, 0) for the end (or for
  * a piece that starts at W).  The same num_splits must be passed to
- * paged_mqa_logits.  Requires 1 <= batch <= 16384, 1 <= next_n <= 4,
+ * paged_mqa_logits.  Requires 1 <= batch <= 8192, 1 <= next_n <= 16,
  * block_size in {16, 32, 64}, 1 <= num_splits <= 65536.
  */
 int64_t paged_mqa_logits_metadata_size(int32_t num_splits);  /* int32 count */

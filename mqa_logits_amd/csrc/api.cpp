@@ -253,7 +253,7 @@ int64_t paged_mqa_logits_metadata_size(int32_t num_splits) {
 static mqa_status check_paged_shape(int32_t batch, int32_t next_n, int32_t block_size,
                                     int32_t max_context_len, int32_t num_splits, const char* who) {
   if (batch < 1 || batch > 8192) return fail(MQA_ERR_UNSUPPORTED, "%s: batch=%d not in [1, 8192]", who, batch);
-  if (next_n < 1 || next_n > 4) return fail(MQA_ERR_UNSUPPORTED, "%s: next_n=%d not in [1, 4]", who, next_n);
+  if (next_n < 1 || next_n > 16) return fail(MQA_ERR_UNSUPPORTED, "%s: next_n=%d not in [1, 16]", who, next_n);
   if (block_size != 16 && block_size != 32 && block_size != 64)
     return fail(MQA_ERR_UNSUPPORTED, "%s: block_size=%d not in {16, 32, 64}", who, block_size);
   if (max_context_len < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative max_context_len", who);

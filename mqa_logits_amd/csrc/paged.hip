@@ -8,10 +8,11 @@
 // made once per decoding step splits the (sequence, KV block) work list over
 // the workers (same PR, a97b74d Root cause / Fix).
 //
-// A worker is one wave.  Its 4 query rows are the next_n (<= 4) tokens of the
-// sequence it is on, so one unit = one KV block for all of a sequence's rows
-// (a single query atom: producer and consumer of the schedule cannot
-// disagree on atoms).  Columns past a sequence's last block are -inf fill
+// A worker is one wave.  One unit = one KV block for all next_n query rows of
+// a sequence (a single query atom: producer and consumer of the schedule
+// cannot disagree on atoms).  The wave holds 4 query rows at a time, so for
+// next_n > 4 it walks its run of blocks once per group of 4 rows; the re-read
+// blocks come from L2.  Columns past a sequence's last block are -inf fill
 // units spread round-robin over the workers in the same launch.
 #include "common.hpp"
 #include "launch.hpp"
@@ -32,13 +33,11 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
   const int worker = blockIdx.x;                // one wave per block
   if (worker >= p.num_splits) return;
 
-  const int g = lane >> 4;                 // output row (query token) of this lane
+  const int g = lane >> 4;                 // output row (query token) of this lane in its group
   const int n = lane & 15;                 // column within a 16-token tile
   const int kb = lane >> 4;                // lane group: operand pieces and scale block
   const bool kb_ok = L::scale_ok(kb);
-  const bool row_ok = g < p.next_n;
-  const int t_e = min(g, p.next_n - 1);
-  const int t_a = min((lane >> 2) & 3, p.next_n - 1);
+  const int n_groups = (p.next_n + kRowsPerWave - 1) / kRowsPerWave;
   const int bs = p.bs;
   const int bs_shift = 31 - __builtin_clz(bs);
 
@@ -73,65 +72,71 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
     // this worker's blocks of sequence b: [blk, seg_end)
     const int seg_end = b < eb ? n_b : min(n_b, eblk);
     const int64_t r0 = (int64_t)b * p.next_n;
-    rg.load(p.q, p.q_sf, p.w, r0 + t_a, r0 + t_e, lane);
-    const int e_tok = clampi(ctx - p.next_n + t_e + 1, 0, len);   // this lane's row end
-    const Rsrc out_r = make_rsrc(p.out + r0 * p.stride,
-                                 (uint32_t)(p.next_n * p.stride * 4));
-    const int lane_off = (t_e * (int)p.stride + n) * 4;
-    const int rel_n = n - e_tok;           // j0 + rel_n < 0  iff  column in range
+    for (int grp = 0; grp < n_groups; ++grp) {
+      const int t0 = grp * kRowsPerWave;
+      const bool row_ok = t0 + g < p.next_n;
+      const int t_e = min(t0 + g, p.next_n - 1);
+      const int t_a = min(t0 + ((lane >> 2) & 3), p.next_n - 1);
+      rg.load(p.q, p.q_sf, p.w, r0 + t_a, r0 + t_e, lane);
+      const int e_tok = clampi(ctx - p.next_n + t_e + 1, 0, len);   // this lane's row end
+      const Rsrc out_r = make_rsrc(p.out + r0 * p.stride,
+                                   (uint32_t)(p.next_n * p.stride * 4));
+      const int lane_off = (t_e * (int)p.stride + n) * 4;
+      const int rel_n = n - e_tok;           // j0 + rel_n < 0  iff  column in range
 
-    for (int sub = blk; sub < seg_end; sub += kBtWindow) {
-      const int cnt = min(kBtWindow, seg_end - sub);
-      const int bt_lane = clampi(p.bt[(int64_t)b * p.bt_stride + sub + min(lane, cnt - 1)], 0,
-                                 p.num_blocks - 1);
-      const int col0 = sub << bs_shift;
-      const int col1 = min((sub + cnt) << bs_shift, p.max_ctx);
-      const int wlim_n = (row_ok ? col1 : 0) - n;
+      for (int sub = blk; sub < seg_end; sub += kBtWindow) {
+        const int cnt = min(kBtWindow, seg_end - sub);
+        const int bt_lane = clampi(p.bt[(int64_t)b * p.bt_stride + sub + min(lane, cnt - 1)], 0,
+                                   p.num_blocks - 1);
+        const int col0 = sub << bs_shift;
+        const int col1 = min((sub + cnt) << bs_shift, p.max_ctx);
+        const int wlim_n = (row_ok ? col1 : 0) - n;
 
-      auto load = [&](int j0, KvOp& o) {
-        const int bi = min((j0 >> bs_shift) - sub, cnt - 1);
-        const int pblk = __builtin_amdgcn_readlane(bt_lane, bi);
-        const int tok = (pblk << bs_shift) + (j0 & (bs - 1));   // first pool token of the step
-        const Rsrc kv_r = make_rsrc(p.kv + (int64_t)tok * kRowBytes, kTileN * kRowBytes);
-        o.b = buffer_operand(kv_r, b_lo, b_hi);
-        if constexpr (FmtInfo<FMT>::kMX) {
-          o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, (tok + n) * kNKB + kb, 0, 0)
-                       : 127;
-          o.ks = 1.f;
-        } else {
-          o.bs = 127;
-          o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, (tok + n) * 4, 0, 0));
-        }
-      };
-      // Paged decode is bound by the KV gather, so FP8 always takes the
-      // sign-exact path (negative token scales negate the token's codes)
-      // instead of scanning the scales first.
-      constexpr bool kFlip = !FmtInfo<FMT>::kMX;
-      KvOp o[kKvStages];
-      prefetch_span(col0, o, load);
-      if constexpr (CLEAN) {
-        // Whole 16-byte groups of the window through LDS (lane l: row l / 16,
-        // columns 4 (l % 16) .. +3 of a trip); in range iff column < e_tok.
-        const int lim = col1 & ~3;
-        const int last_j0 = row_ok ? lim - 4 * n - 4 : -0x40000000;
-        StagedSink sink{stage, out_r, col0, g * kTripCols + n, g * kTripCols + 4 * n,
-                        (t_e * (int)p.stride + 4 * n) * 4, last_j0, n, e_tok, ninf4, kOOB};
-        const int walked = compute_span<kFlip>(rg, col0, col1, o, load, sink);
-        if ((col1 & 3) != 0) {             // max_ctx not a multiple of 4: 1..3 columns
-          const int gs = col1 & ~3, jt = walked - kTripCols;
-          if (row_ok && gs + n < col1) {
-            float v = neg_inf();
-            if (gs >= jt && gs < walked) v = sink.buffer(jt)[g * kTripCols + (gs - jt) + n];
-            buffer_store_nt(out_r, (t_e * (int)p.stride + gs + n) * 4, v);
+        auto load = [&](int j0, KvOp& o) {
+          const int bi = min((j0 >> bs_shift) - sub, cnt - 1);
+          const int pblk = __builtin_amdgcn_readlane(bt_lane, bi);
+          const int tok = (pblk << bs_shift) + (j0 & (bs - 1));   // first pool token of the step
+          const Rsrc kv_r = make_rsrc(p.kv + (int64_t)tok * kRowBytes, kTileN * kRowBytes);
+          o.b = buffer_operand(kv_r, b_lo, b_hi);
+          if constexpr (FmtInfo<FMT>::kMX) {
+            o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, (tok + n) * kNKB + kb, 0, 0)
+                         : 127;
+            o.ks = 1.f;
+          } else {
+            o.bs = 127;
+            o.ks = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sc_r, (tok + n) * 4, 0, 0));
           }
-        }
-      } else {
-        auto off = [&](int j0, float& v) {
-          (void)v;
-          return (j0 < wlim_n && j0 + rel_n < 0) ? lane_off + 4 * j0 : kOOB;
         };
-        DwordSink<decltype(off)> sink{out_r, off, col0};
-        compute_span<kFlip>(rg, col0, col1, o, load, sink);
+        // Paged decode is bound by the KV gather, so FP8 always takes the
+        // sign-exact path (negative token scales negate the token's codes)
+        // instead of scanning the scales first.
+        constexpr bool kFlip = !FmtInfo<FMT>::kMX;
+        KvOp o[kKvStages];
+        prefetch_span(col0, o, load);
+        if constexpr (CLEAN) {
+          // Whole 16-byte groups of the window through LDS (lane l: row l / 16,
+          // columns 4 (l % 16) .. +3 of a trip); in range iff column < e_tok.
+          const int lim = col1 & ~3;
+          const int last_j0 = row_ok ? lim - 4 * n - 4 : -0x40000000;
+          StagedSink sink{stage, out_r, col0, g * kTripCols + n, g * kTripCols + 4 * n,
+                          (t_e * (int)p.stride + 4 * n) * 4, last_j0, n, e_tok, ninf4, kOOB};
+          const int walked = compute_span<kFlip>(rg, col0, col1, o, load, sink);
+          if ((col1 & 3) != 0) {             // max_ctx not a multiple of 4: 1..3 columns
+            const int gs = col1 & ~3, jt = walked - kTripCols;
+            if (row_ok && gs + n < col1) {
+              float v = neg_inf();
+              if (gs >= jt && gs < walked) v = sink.buffer(jt)[g * kTripCols + (gs - jt) + n];
+              buffer_store_nt(out_r, (t_e * (int)p.stride + gs + n) * 4, v);
+            }
+          }
+        } else {
+          auto off = [&](int j0, float& v) {
+            (void)v;
+            return (j0 < wlim_n && j0 + rel_n < 0) ? lane_off + 4 * j0 : kOOB;
+          };
+          DwordSink<decltype(off)> sink{out_r, off, col0};
+          compute_span<kFlip>(rg, col0, col1, o, load, sink);
+        }
       }
     }
     blk = seg_end;
@@ -147,14 +152,18 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
       if (c < ((len + bs - 1) >> bs_shift)) continue;
       const Rsrc out_r = make_rsrc(p.out + (int64_t)fb * p.next_n * p.stride,
                                    (uint32_t)(p.next_n * p.stride * 4));
-      // 16-byte groups (lane l: row l / 16, columns 4 (l % 16) .. +3), then
-      // the 1..3 columns of a last group cut by max_ctx
-      const int grp_off = (t_e * (int)p.stride + 4 * n) * 4;
+      // 16-byte groups (lane l: row l / 16 of a 4-row group, columns
+      // 4 (l % 16) .. +3), then the 1..3 columns of a last group cut by max_ctx
       const int c1 = min((c + 1) << bs_shift, p.max_ctx);
-      for (int j0 = c << bs_shift; j0 < c1; j0 += kTripCols)
-        buffer_store4_nt(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + 4 * j0 : kOOB, ninf4);
-      if ((c1 & 3) != 0 && row_ok && (c1 & ~3) + n < c1 && (c1 & ~3) >= (c << bs_shift))
-        buffer_store_nt(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * 4, neg_inf());
+      for (int t0 = 0; t0 < p.next_n; t0 += kRowsPerWave) {
+        const bool row_ok = t0 + g < p.next_n;
+        const int t_e = min(t0 + g, p.next_n - 1);
+        const int grp_off = (t_e * (int)p.stride + 4 * n) * 4;
+        for (int j0 = c << bs_shift; j0 < c1; j0 += kTripCols)
+          buffer_store4_nt(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + 4 * j0 : kOOB, ninf4);
+        if ((c1 & 3) != 0 && row_ok && (c1 & ~3) + n < c1 && (c1 & ~3) >= (c << bs_shift))
+          buffer_store_nt(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * 4, neg_inf());
+      }
     }
   }
 }

@@ -109,7 +109,7 @@ def paged_meta_args(**kw):
 @pytest.mark.parametrize("change,expect", [
     (dict(batch=0), UNSUPPORTED),
     (dict(batch=9000), UNSUPPORTED),
-    (dict(next_n=5), UNSUPPORTED),
+    (dict(next_n=17), UNSUPPORTED),
     (dict(next_n=0), UNSUPPORTED),
     (dict(bs=128), UNSUPPORTED),
     (dict(bs=48), UNSUPPORTED),
@@ -138,7 +138,7 @@ def paged_args(**kw):
     (dict(bt=None), INVALID),
     (dict(sched=None), INVALID),
     (dict(h=24), UNSUPPORTED),
-    (dict(next_n=6), UNSUPPORTED),
+    (dict(next_n=20), UNSUPPORTED),
     (dict(kvs=None), INVALID),
 ])
 def test_paged_validation(change, expect):
