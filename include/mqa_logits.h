@@ -69,13 +69,26 @@ typedef enum {
 } mqa_dtype;
 
 /*
+ * Element type of the weights and of the logits ("[PR #435] Improve SM100 MX
+ * MQA logits clean-output performance", Validation: FP32 and BF16 weights and
+ * output; the logits_dtype argument of its reproducer).  The arithmetic is
+ * fp32 either way: bf16 weights are widened exactly, and bf16 logits are the
+ * fp32 results rounded to nearest (ties to even); -inf stays -inf.
+ */
+typedef enum {
+  MQA_F32 = 0,
+  MQA_BF16 = 1
+} mqa_float;
+
+/*
  * Dense logits ("Implementing Standard MQA Logits Computation" in the DeepGEMM
  * MQA-logits article; the clean_logits flag of the reproducer in PR #435).
  *   q        [Sq, H, D] (fp4: [Sq, H, D/2])      q_sf  [Sq, H, D/32] or NULL
  *   kv       [Skv, D]   (fp4: [Skv, D/2])        kv_sf [Skv, D/32]  or NULL
  *   kv_scale [Skv] fp32 for MQA_FP8_E4M3, NULL for MX formats
- *   weights  [Sq, H] fp32;  k_start, k_end [Sq] int32
- *   logits   [Sq, logits_stride] fp32, logits_stride >= Skv.  Columns
+ *   weights  [Sq, H] of weights_type;  k_start, k_end [Sq] int32
+ *   logits   [Sq, logits_stride] of logits_type, logits_stride >= Skv (even
+ *            for bf16; the pointer 4-byte aligned).  Columns
  *            [Skv, logits_stride) are never written.
  *   clean_logits != 0: entries outside a row's range are written as -inf;
  *   clean_logits == 0: they are left untouched.
@@ -84,11 +97,12 @@ typedef enum {
 mqa_status mqa_logits(mqa_dtype dt,
                       const void* q, const uint8_t* q_sf,
                       const void* kv, const uint8_t* kv_sf,
-                      const float* kv_scale, const float* weights,
+                      const float* kv_scale, const void* weights,
                       const int32_t* k_start, const int32_t* k_end,
-                      float* logits, int64_t logits_stride,
+                      void* logits, int64_t logits_stride,
                       int32_t sq, int32_t skv, int32_t h, int32_t d,
-                      int32_t clean_logits, hipStream_t stream);
+                      int32_t clean_logits, mqa_float weights_type, mqa_float logits_type,
+                      hipStream_t stream);
 
 /*
  * Row offsets of the compressed layout ("Compressed Logits" in the DeepGEMM
@@ -103,15 +117,17 @@ mqa_status mqa_logits_compressed_offsets(const int32_t* k_start, const int32_t* 
 /*
  * Compressed logits: entry (i, j), s_i <= j < e_i, is written to
  * logits_packed[row_offsets[i] + (j - s_i)]; nothing else is written.
- * logits_packed holds row_offsets[Sq] floats.  Other arguments as mqa_logits.
+ * logits_packed holds row_offsets[Sq] elements of logits_type (aligned to
+ * the element size).  Other arguments as mqa_logits.
  */
 mqa_status mqa_logits_compressed(mqa_dtype dt,
                                  const void* q, const uint8_t* q_sf,
                                  const void* kv, const uint8_t* kv_sf,
-                                 const float* kv_scale, const float* weights,
+                                 const float* kv_scale, const void* weights,
                                  const int32_t* k_start, const int32_t* k_end,
-                                 const int64_t* row_offsets, float* logits_packed,
+                                 const int64_t* row_offsets, void* logits_packed,
                                  int32_t sq, int32_t skv, int32_t h, int32_t d,
+                                 mqa_float weights_type, mqa_float logits_type,
                                  hipStream_t stream);
 
 /*
@@ -145,28 +161,30 @@ mqa_status paged_mqa_logits_metadata(const int32_t* context_lens, int32_t batch,
  *   kv_pool  [num_blocks, block_size, D] (fp4: D/2 bytes)
  *   kv_sf_pool [num_blocks, block_size, D/32] or NULL
  *   kv_scale_pool [num_blocks, block_size] fp32 (FP8 only, else NULL)
- *   weights  [batch*next_n, H] fp32
+ *   weights  [batch*next_n, H] of weights_type
  *   context_lens [batch] int32: tokens of sequence b including its next_n new
  *            ones; logical token j of b is slot j % block_size of physical
  *            block block_table[b * block_table_stride + j / block_size]
  *   schedule from paged_mqa_logits_metadata with the same arguments
- *   logits   [batch*next_n, logits_stride] fp32, logits_stride >=
- *            max_context_len.  Row b*next_n + t covers keys
+ *   logits   [batch*next_n, logits_stride] of logits_type, logits_stride >=
+ *            max_context_len (even for bf16; the pointer 4-byte aligned).
+ *            Row b*next_n + t covers keys
  *            [0, clamp(ctx_b - next_n + t + 1, 0, min(ctx_b, max_context_len)));
  *            with clean_logits the rest of [0, max_context_len) is -inf.
  */
 mqa_status paged_mqa_logits(mqa_dtype dt,
                             const void* q, const uint8_t* q_sf,
                             const void* kv_pool, const uint8_t* kv_sf_pool,
-                            const float* kv_scale_pool, const float* weights,
+                            const float* kv_scale_pool, const void* weights,
                             const int32_t* context_lens,
                             const int32_t* block_table, int64_t block_table_stride,
                             const int32_t* schedule,
-                            float* logits, int64_t logits_stride,
+                            void* logits, int64_t logits_stride,
                             int32_t batch, int32_t next_n, int32_t h, int32_t d,
                             int32_t block_size, int32_t num_blocks,
                             int32_t max_context_len, int32_t num_splits,
-                            int32_t clean_logits, hipStream_t stream);
+                            int32_t clean_logits, mqa_float weights_type,
+                            mqa_float logits_type, hipStream_t stream);
 
 /* Compute units of a device (the get_num_sms analogue of the DeepGEMM
  * article's paged example); negative on error. */

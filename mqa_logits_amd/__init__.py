@@ -24,6 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmqa_logits.so")
 
 FORMATS = {"fp8": 0, "mxfp8": 1, "mxfp4": 2}
+# mqa_float of the C ABI: element type of the weights and of the logits
+FLOAT_TYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
 class MqaError(RuntimeError):
@@ -42,12 +44,13 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sigs = {
-        "mqa_logits": [I32, P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, I32, P],
+        "mqa_logits": [I32, P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, I32, P],
         "mqa_logits_compressed_offsets": [P, P, I32, I32, P, P],
-        "mqa_logits_compressed": [I32, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, P],
+        "mqa_logits_compressed": [I32, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                  P],
         "paged_mqa_logits_metadata": [P, I32, I32, I32, I32, I32, P, P],
         "paged_mqa_logits": [I32, P, P, P, P, P, P, P, P, I64, P, P, I64,
-                             I32, I32, I32, I32, I32, I32, I32, I32, I32, P],
+                             I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, P],
     }
     for name, argtypes in sigs.items():
         fn = getattr(lib, name)
@@ -99,6 +102,19 @@ def _head_dim(fmt, q):
     return q.shape[-1] * (2 if fmt == "mxfp4" else 1)
 
 
+def _float_type(dtype, what):
+    if dtype not in FLOAT_TYPES:
+        raise ValueError(f"{what} must be float32 or bfloat16, got {dtype}")
+    return FLOAT_TYPES[dtype]
+
+
+def _logits_rows(rows, cols, dtype, device):
+    """[rows, cols] logits; bf16 rows get an even stride (the C ABI needs one)."""
+    width = cols + (cols & 1) if dtype == torch.bfloat16 else cols
+    out = torch.empty(rows, width, dtype=dtype, device=device)
+    return out[:, :cols] if width != cols else out
+
+
 def mqa_num_cus(device=0):
     n = lib.mqa_num_cus(int(device))
     if n < 0:
@@ -114,19 +130,21 @@ def paged_mqa_logits_default_splits(device=0):
 
 
 def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
-               clean_logits=True, out=None):
-    """Dense logits [Sq, Skv] fp32 (out may be a wider-strided row view)."""
+               clean_logits=True, out=None, logits_dtype=torch.float32):
+    """Dense logits [Sq, Skv] of logits_dtype (out may be a wider-strided row
+    view; its dtype then decides).  weights: float32 or bfloat16."""
     sq, h = weights.shape
     skv = kv.shape[0]
     if out is None:
-        out = torch.empty(sq, skv, dtype=torch.float32, device=q.device)
+        out = _logits_rows(sq, skv, logits_dtype, q.device)
     if out.stride(1) != 1:
         raise ValueError("logits rows must be contiguous")
     _check(lib.mqa_logits(
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv), _ptr(kv_sf), _ptr(kv_scale),
         _ptr(weights), _ptr(k_start), _ptr(k_end), ctypes.c_void_p(out.data_ptr()),
         out.stride(0) if sq > 0 else skv, sq, skv, h, _head_dim(fmt, q),
-        1 if clean_logits else 0, _stream(q)))
+        1 if clean_logits else 0, _float_type(weights.dtype, "weights"),
+        _float_type(out.dtype, "logits"), _stream(q)))
     return out
 
 
@@ -141,8 +159,9 @@ def mqa_logits_compressed_offsets(k_start, k_end, skv, out=None):
 
 
 def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
-                          row_offsets=None, out=None):
-    """Packed logits; returns (packed fp32 [total], row_offsets int64 [Sq+1]).
+                          row_offsets=None, out=None, logits_dtype=torch.float32):
+    """Packed logits; returns (packed [total] of logits_dtype, row_offsets int64
+    [Sq+1]).
 
     Without `out`, the total length is read back from the device (a sync)."""
     sq, h = weights.shape
@@ -150,11 +169,12 @@ def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k
     if row_offsets is None:
         row_offsets = mqa_logits_compressed_offsets(k_start, k_end, skv)
     if out is None:
-        out = torch.empty(int(row_offsets[-1].item()), dtype=torch.float32, device=q.device)
+        out = torch.empty(int(row_offsets[-1].item()), dtype=logits_dtype, device=q.device)
     _check(lib.mqa_logits_compressed(
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv), _ptr(kv_sf), _ptr(kv_scale),
         _ptr(weights), _ptr(k_start), _ptr(k_end), _ptr(row_offsets), _ptr(out),
-        sq, skv, h, _head_dim(fmt, q), _stream(q)))
+        sq, skv, h, _head_dim(fmt, q), _float_type(weights.dtype, "weights"),
+        _float_type(out.dtype, "logits"), _stream(q)))
     return out, row_offsets
 
 
@@ -173,14 +193,14 @@ def paged_mqa_logits_metadata(context_lens, next_n, block_size, max_context_len,
 
 def paged_mqa_logits(fmt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
                      context_lens, block_table, schedule, next_n, max_context_len,
-                     clean_logits=True, out=None):
-    """Paged decode logits [batch * next_n, max_context_len] fp32."""
+                     clean_logits=True, out=None, logits_dtype=torch.float32):
+    """Paged decode logits [batch * next_n, max_context_len] of logits_dtype."""
     batch = context_lens.shape[0]
     rows, h = weights.shape
     num_blocks, block_size = kv_pool.shape[0], kv_pool.shape[1]
     num_splits = schedule.shape[0] - 1
     if out is None:
-        out = torch.empty(rows, max_context_len, dtype=torch.float32, device=q.device)
+        out = _logits_rows(rows, max_context_len, logits_dtype, q.device)
     if out.stride(1) != 1:
         raise ValueError("logits rows must be contiguous")
     _check(lib.paged_mqa_logits(
@@ -188,5 +208,6 @@ def paged_mqa_logits(fmt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
         _ptr(weights), _ptr(context_lens), _ptr(block_table), block_table.stride(0),
         _ptr(schedule), ctypes.c_void_p(out.data_ptr()), out.stride(0), batch, next_n, h,
         _head_dim(fmt, q), block_size, num_blocks, max_context_len, num_splits,
-        1 if clean_logits else 0, _stream(q)))
+        1 if clean_logits else 0, _float_type(weights.dtype, "weights"),
+        _float_type(out.dtype, "logits"), _stream(q)))
     return out

@@ -56,10 +56,15 @@ bool debug_enabled() {
 
 // Shared checks of the element formats and head shape.
 mqa_status check_common(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
-                        const uint8_t* kv_sf, const float* kv_scale, const float* weights,
-                        int32_t h, int32_t d, const char* who) {
+                        const uint8_t* kv_sf, const float* kv_scale, const void* weights,
+                        mqa_float weights_type, mqa_float logits_type, int32_t h, int32_t d,
+                        const char* who) {
   if (dt != MQA_FP8_E4M3 && dt != MQA_MXFP8_E4M3 && dt != MQA_MXFP4_E2M1)
     return fail(MQA_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dt);
+  if (weights_type != MQA_F32 && weights_type != MQA_BF16)
+    return fail(MQA_ERR_INVALID_ARG, "%s: unknown weights type %d", who, (int)weights_type);
+  if (logits_type != MQA_F32 && logits_type != MQA_BF16)
+    return fail(MQA_ERR_INVALID_ARG, "%s: unknown logits type %d", who, (int)logits_type);
   if (h != 8 && h != 16 && h != 32 && h != 64)
     return fail(MQA_ERR_UNSUPPORTED, "%s: H=%d not supported (8, 16, 32, 64)", who, h);
   if (d != 64 && d != 128)
@@ -124,15 +129,16 @@ hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
 // sum's pieces (qsum.hip), written into the stream's workspace right before
 // the launch that reads them.
 template <class Launch>
-mqa_status with_qsum(mqa_dtype dt, const void* q, const uint8_t* q_sf, const float* weights,
-                     int32_t rows, int32_t d, const uint8_t** ql, const uint8_t** ql_sf,
-                     hipStream_t stream, const char* who, Launch&& launch) {
+mqa_status with_qsum(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* weights,
+                     int32_t w_bf16, int32_t rows, int32_t d, const uint8_t** ql,
+                     const uint8_t** ql_sf, hipStream_t stream, const char* who,
+                     Launch&& launch) {
   const size_t ql_bytes = (size_t)rows * 4 * d, sf_bytes = (size_t)rows * 4 * (d / 32);
   void* ws = nullptr;
   hipError_t e = workspace(stream, ql_bytes + sf_bytes + 16, &ws);
   if (e != hipSuccess) return hip_status(e, who);
   mqa::QsumParams qp{static_cast<const uint8_t*>(q), q_sf, weights, static_cast<uint8_t*>(ws),
-                     static_cast<uint8_t*>(ws) + ql_bytes, rows};
+                     static_cast<uint8_t*>(ws) + ql_bytes, rows, w_bf16};
   *ql = qp.ql;
   *ql_sf = qp.ql_sf;
   e = mqa::launch_qsum((int)dt, d, qp, stream);
@@ -141,10 +147,11 @@ mqa_status with_qsum(mqa_dtype dt, const void* q, const uint8_t* q_sf, const flo
 }
 
 mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
-                     const uint8_t* kv_sf, const float* kv_scale, const float* weights,
-                     const int32_t* k_start, const int32_t* k_end, const int64_t* row_off,
-                     float* out, int64_t stride, int32_t sq, int32_t skv, int32_t h, int32_t d,
-                     int store, hipStream_t stream, const char* who) {
+                     const uint8_t* kv_sf, const float* kv_scale, const void* weights,
+                     mqa_float weights_type, const int32_t* k_start, const int32_t* k_end,
+                     const int64_t* row_off, void* out, mqa_float logits_type, int64_t stride,
+                     int32_t sq, int32_t skv, int32_t h, int32_t d, int store,
+                     hipStream_t stream, const char* who) {
   const int64_t row_bytes = (dt == MQA_MXFP4_E2M1 ? d / 2 : d);
   if ((int64_t)skv * row_bytes >= kMaxRangeBytes || (int64_t)skv * 16 >= kMaxRangeBytes)
     return fail(MQA_ERR_UNSUPPORTED, "%s: Skv=%d too large", who, skv);
@@ -163,15 +170,19 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   p.sq = sq;
   p.skv = skv;
   p.n_chunks = pick_chunks(sq, skv);
+  p.w_bf16 = weights_type == MQA_BF16;
+  const int out_type = logits_type == MQA_BF16 ? mqa::kBF16 : mqa::kF32;
   const int64_t grid = (int64_t)((sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves)) * p.n_chunks;
   if (grid > 0x7fffffff) return fail(MQA_ERR_UNSUPPORTED, "%s: problem too large", who);
   if (debug_enabled())
-    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d store=%d Sq=%d Skv=%d chunks=%d grid=%lld\n",
-            who, (int)dt, h, d, store, sq, skv, p.n_chunks, (long long)grid);
+    fprintf(stderr,
+            "[mqa_logits] %s dt=%d H=%d D=%d store=%d w=%d out=%d Sq=%d Skv=%d chunks=%d grid=%lld\n",
+            who, (int)dt, h, d, store, (int)weights_type, (int)logits_type, sq, skv, p.n_chunks,
+            (long long)grid);
   if (h != mqa::kLinHeads)
-    return hip_status(mqa::launch_dense((int)dt, h, d, store, p, stream), who);
-  return with_qsum(dt, q, q_sf, weights, sq, d, &p.ql, &p.ql_sf, stream, who,
-                   [&] { return mqa::launch_dense((int)dt, h, d, store, p, stream); });
+    return hip_status(mqa::launch_dense((int)dt, h, d, store, out_type, p, stream), who);
+  return with_qsum(dt, q, q_sf, weights, p.w_bf16, sq, d, &p.ql, &p.ql_sf, stream, who,
+                   [&] { return mqa::launch_dense((int)dt, h, d, store, out_type, p, stream); });
 }
 
 }  // namespace
@@ -196,24 +207,28 @@ int32_t paged_mqa_logits_default_splits(int32_t device) {
 }
 
 mqa_status mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
-                      const uint8_t* kv_sf, const float* kv_scale, const float* weights,
-                      const int32_t* k_start, const int32_t* k_end, float* logits,
+                      const uint8_t* kv_sf, const float* kv_scale, const void* weights,
+                      const int32_t* k_start, const int32_t* k_end, void* logits,
                       int64_t logits_stride, int32_t sq, int32_t skv, int32_t h, int32_t d,
-                      int32_t clean_logits, hipStream_t stream) {
+                      int32_t clean_logits, mqa_float weights_type, mqa_float logits_type,
+                      hipStream_t stream) {
   const char* who = "mqa_logits";
   if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
   if (logits_stride < skv) return fail(MQA_ERR_INVALID_ARG, "%s: logits_stride < Skv", who);
   if (sq == 0 || skv == 0) return ok();
-  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, h, d, who);
+  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type,
+                               logits_type, h, d, who);
   if (st != MQA_OK) return st;
   if (!k_start || !k_end || !logits) return fail(MQA_ERR_INVALID_ARG, "%s: null ranges or logits", who);
   if (!aligned(k_start, 4) || !aligned(k_end, 4) || !aligned(logits, 4))
     return fail(MQA_ERR_INVALID_ARG, "%s: ranges or logits misaligned", who);
+  if (logits_type == MQA_BF16 && (logits_stride & 1))
+    return fail(MQA_ERR_INVALID_ARG, "%s: bf16 logits need an even logits_stride", who);
   if (logits_stride * 4 * 4 >= kMaxRangeBytes)
     return fail(MQA_ERR_UNSUPPORTED, "%s: logits_stride %lld too large", who, (long long)logits_stride);
-  return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, nullptr, logits,
-                   logits_stride, sq, skv, h, d, clean_logits ? mqa::kDenseClean : mqa::kDenseKeep,
-                   stream, who);
+  return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type, k_start, k_end,
+                   nullptr, logits, logits_type, logits_stride, sq, skv, h, d,
+                   clean_logits ? mqa::kDenseClean : mqa::kDenseKeep, stream, who);
 }
 
 mqa_status mqa_logits_compressed_offsets(const int32_t* k_start, const int32_t* k_end, int32_t sq,
@@ -228,22 +243,25 @@ mqa_status mqa_logits_compressed_offsets(const int32_t* k_start, const int32_t* 
 }
 
 mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
-                                 const uint8_t* kv_sf, const float* kv_scale, const float* weights,
+                                 const uint8_t* kv_sf, const float* kv_scale, const void* weights,
                                  const int32_t* k_start, const int32_t* k_end,
-                                 const int64_t* row_offsets, float* logits_packed, int32_t sq,
-                                 int32_t skv, int32_t h, int32_t d, hipStream_t stream) {
+                                 const int64_t* row_offsets, void* logits_packed, int32_t sq,
+                                 int32_t skv, int32_t h, int32_t d, mqa_float weights_type,
+                                 mqa_float logits_type, hipStream_t stream) {
   const char* who = "mqa_logits_compressed";
   if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
   if (sq == 0 || skv == 0) return ok();
-  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, h, d, who);
+  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type,
+                               logits_type, h, d, who);
   if (st != MQA_OK) return st;
   if (!k_start || !k_end || !row_offsets || !logits_packed)
     return fail(MQA_ERR_INVALID_ARG, "%s: null ranges, offsets or output", who);
   if (!aligned(k_start, 4) || !aligned(k_end, 4) || !aligned(row_offsets, 8) ||
-      !aligned(logits_packed, 4))
+      !aligned(logits_packed, logits_type == MQA_BF16 ? 2 : 4))
     return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
-  return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, row_offsets,
-                   logits_packed, 0, sq, skv, h, d, mqa::kCompressed, stream, who);
+  return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type, k_start, k_end,
+                   row_offsets, logits_packed, logits_type, 0, sq, skv, h, d, mqa::kCompressed,
+                   stream, who);
 }
 
 int64_t paged_mqa_logits_metadata_size(int32_t num_splits) {
@@ -281,16 +299,18 @@ mqa_status paged_mqa_logits_metadata(const int32_t* context_lens, int32_t batch,
 
 mqa_status paged_mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv_pool,
                             const uint8_t* kv_sf_pool, const float* kv_scale_pool,
-                            const float* weights, const int32_t* context_lens,
+                            const void* weights, const int32_t* context_lens,
                             const int32_t* block_table, int64_t block_table_stride,
-                            const int32_t* schedule, float* logits, int64_t logits_stride,
+                            const int32_t* schedule, void* logits, int64_t logits_stride,
                             int32_t batch, int32_t next_n, int32_t h, int32_t d,
                             int32_t block_size, int32_t num_blocks, int32_t max_context_len,
-                            int32_t num_splits, int32_t clean_logits, hipStream_t stream) {
+                            int32_t num_splits, int32_t clean_logits, mqa_float weights_type,
+                            mqa_float logits_type, hipStream_t stream) {
   const char* who = "paged_mqa_logits";
   mqa_status st = check_paged_shape(batch, next_n, block_size, max_context_len, num_splits, who);
   if (st != MQA_OK) return st;
-  st = check_common(dt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights, h, d, who);
+  st = check_common(dt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights, weights_type,
+                    logits_type, h, d, who);
   if (st != MQA_OK) return st;
   if (num_blocks < 1) return fail(MQA_ERR_INVALID_ARG, "%s: num_blocks < 1", who);
   if (!context_lens || !block_table || !schedule || !logits)
@@ -303,6 +323,8 @@ mqa_status paged_mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, co
   if (!aligned(context_lens, 4) || !aligned(block_table, 4) || !aligned(schedule, 4) ||
       !aligned(logits, 4))
     return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  if (logits_type == MQA_BF16 && (logits_stride & 1))
+    return fail(MQA_ERR_INVALID_ARG, "%s: bf16 logits need an even logits_stride", who);
   if ((int64_t)next_n * logits_stride * 4 >= kMaxRangeBytes)
     return fail(MQA_ERR_UNSUPPORTED, "%s: logits_stride %lld too large", who, (long long)logits_stride);
   if ((int64_t)num_blocks * block_size * 4 >= kMaxRangeBytes)
@@ -328,10 +350,13 @@ mqa_status paged_mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, co
   p.max_ctx = max_context_len;
   p.num_splits = num_splits;
   p.nb_max = (int32_t)nb_max;
+  p.w_bf16 = weights_type == MQA_BF16;
   if (debug_enabled())
     fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d batch=%d next_n=%d bs=%d splits=%d\n", who,
             (int)dt, h, d, batch, next_n, block_size, num_splits);
-  return hip_status(mqa::launch_paged((int)dt, h, d, clean_logits ? 1 : 0, p, stream), who);
+  const int out_type = logits_type == MQA_BF16 ? mqa::kBF16 : mqa::kF32;
+  return hip_status(mqa::launch_paged((int)dt, h, d, clean_logits ? 1 : 0, out_type, p, stream),
+                    who);
 }
 
 }  // extern "C"

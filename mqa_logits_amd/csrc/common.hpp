@@ -144,6 +144,40 @@ __device__ __forceinline__ void buffer_store4_nt(Rsrc r, int off, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kNT);
 }
 
+// bf16: the upper half of an fp32 word.  fp32 -> bf16 rounds to nearest even
+// (v_cvt_pk_bf16_f32); bf16 -> fp32 is exact.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int pack_bf16(float a, float b) {
+  return __builtin_bit_cast(int, __builtin_convertvector(v2f{a, b}, v2bf));
+}
+__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Stores of logits elements of type OUT (FloatType) at byte offsets; an
+// offset of kOOB drops the store.
+template <int OUT>
+struct OutElem {
+  static constexpr int kBytes = OUT == kBF16 ? 2 : 4;
+  __device__ static __forceinline__ void store1(Rsrc r, int off, float v) {
+    if constexpr (OUT == kBF16) {
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, off,
+                                            0, kNT);
+    } else {
+      buffer_store_nt(r, off, v);
+    }
+  }
+  // 4 consecutive columns
+  __device__ static __forceinline__ void store4(Rsrc r, int off, float4 v) {
+    if constexpr (OUT == kBF16) {
+      typedef int v2i __attribute__((ext_vector_type(2)));
+      const v2i x = {pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
+      __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, kNT);
+    } else {
+      buffer_store4_nt(r, off, v);
+    }
+  }
+};
+
 // The linear-half tile: A in e4m3 (the weighted query sum's pieces, with
 // their own block scales), B in the KV format.
 template <int FMT>
@@ -174,7 +208,7 @@ struct RowGroup {
   // e_row = the query row whose outputs this lane accumulates (lane >> 4).
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
                                        const uint8_t* __restrict__ q_sf,
-                                       const float* __restrict__ wts, int64_t a_row,
+                                       const void* __restrict__ wts, bool w_bf16, int64_t a_row,
                                        int64_t e_row, int lane) {
     using L = OperandLayout<FMT, D>;
     const int g = lane >> 4;
@@ -200,15 +234,27 @@ struct RowGroup {
     // to the accumulators, weights and streamed KV operands.
 #pragma unroll
     for (int m = 0; m < kMT * kWays; ++m) asm volatile("" : "+a"(qa[m]));
-    const float4* wp = reinterpret_cast<const float4*>(wts + e_row * H);
     constexpr float kW = LIN ? 0.5f : 1.f;
+    if (w_bf16) {
+      const uint2* wp = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(wts) + e_row * H);
 #pragma unroll
-    for (int i = 0; i < H / 4; ++i) {
-      float4 v = wp[i];
-      w[4 * i + 0] = kW * v.x;
-      w[4 * i + 1] = kW * v.y;
-      w[4 * i + 2] = kW * v.z;
-      w[4 * i + 3] = kW * v.w;
+      for (int i = 0; i < H / 4; ++i) {
+        const uint2 v = wp[i];
+        w[4 * i + 0] = kW * bf16_value(v.x & 0xffffu);
+        w[4 * i + 1] = kW * bf16_value(v.x >> 16);
+        w[4 * i + 2] = kW * bf16_value(v.y & 0xffffu);
+        w[4 * i + 3] = kW * bf16_value(v.y >> 16);
+      }
+    } else {
+      const float4* wp = reinterpret_cast<const float4*>(static_cast<const float*>(wts) + e_row * H);
+#pragma unroll
+      for (int i = 0; i < H / 4; ++i) {
+        const float4 v = wp[i];
+        w[4 * i + 0] = kW * v.x;
+        w[4 * i + 1] = kW * v.y;
+        w[4 * i + 2] = kW * v.z;
+        w[4 * i + 3] = kW * v.w;
+      }
     }
   }
 
@@ -370,9 +416,9 @@ __device__ __forceinline__ int compute_span(RG& rg, int cl, int ch, KvOp (&o)[kK
   return end;
 }
 
-// Sink that stores every step's value straight to its output column with a
-// 4-byte store (a per-lane offset of kOOB drops it).
-template <class OffFn>
+// Sink that stores every step's value straight to its output column with
+// one element store (a per-lane offset of kOOB drops it).
+template <int OUT, class OffFn>
 struct DwordSink {
   Rsrc r;
   OffFn off;                                   // (j0, &v) -> byte offset or kOOB; may edit v
@@ -380,7 +426,7 @@ struct DwordSink {
   __device__ __forceinline__ void put(int, int j0, float v) {
     int o = off(j0, v);
     o = j0 >= lo_j0 ? o : kOOB;
-    buffer_store_nt(r, o, v);
+    OutElem<OUT>::store1(r, o, v);
   }
   __device__ __forceinline__ void trip(int) {}
   __device__ __forceinline__ void finish() {}
@@ -389,20 +435,23 @@ struct DwordSink {
 constexpr int kTripCols = kTileN * kKvStages;  // columns per pipeline trip
 static_assert(kTripCols == 64, "StagedSink::buffer() divides by 64");
 
-// Clean output.  A trip's 4 rows x kTripCols columns are staged in LDS
-// and leave as one 16-byte store per lane (lane l: row l / 16, columns
-// 4 (l % 16) .. +3 of the trip), so every row gets whole 256-byte runs
-// instead of a 64-byte piece per step: HBM never has to fetch an output line
-// to merge a partial write.  Trips alternate between two LDS buffers; a
-// trip's group is read back right after its last put and stored one step
-// later, when the read has long returned.
+// Clean output.  A trip's 4 rows x kTripCols columns are staged in LDS (as
+// fp32) and leave as one 4-column store per lane (lane l: row l / 16,
+// columns 4 (l % 16) .. +3 of the trip), so every row gets whole runs of
+// kTripCols elements (256 bytes fp32, 128 bf16) instead of a 16-column piece
+// per step: HBM never has to fetch an output line to merge a partial write.
+// Trips alternate between two LDS buffers; a trip's group is read back right
+// after its last put and stored one step later, when the read has long
+// returned.  OUT: the logits element type (the conversion happens at the
+// store).
+template <int OUT>
 struct StagedSink {
   float* stage;              // 2 x [4][kTripCols] floats in LDS
   Rsrc r;
   int base;                  // first column of the walk (trip-aligned)
   int put_idx;               // this lane's slot: row g, column n of a trip's first step
   int rd_idx;                // this lane's group: row l / 16, column 4 (l % 16)
-  int row_off;               // byte offset of this lane's group in the output, column 0
+  int row_off;               // byte offset of this lane's group in the output at column 0
   int last_j0;               // the group of trip j0 is stored iff base <= j0 <= last_j0
   int rel_n, len;            // column j0 + n is in range iff j0 + rel_n in [0, len)
   float4 pend;               // the last trip read back, and its store offset
@@ -414,15 +463,15 @@ struct StagedSink {
   __device__ __forceinline__ void put(int u, int j0, float v) {
     const bool in_range = (uint32_t)(j0 + rel_n) < (uint32_t)len;
     buffer(j0)[put_idx + u * kTileN] = in_range ? v : neg_inf();
-    if (u == 0) buffer_store4_nt(r, pend_off, pend);
+    if (u == 0) OutElem<OUT>::store4(r, pend_off, pend);
   }
   __device__ __forceinline__ void trip(int jt) {
     asm volatile("" ::: "memory");            // the group read follows every lane's writes
     pend = *reinterpret_cast<const float4*>(buffer(jt) + rd_idx);
-    pend_off = (jt >= base && jt <= last_j0) ? row_off + 4 * jt : kOOB;
+    pend_off = (jt >= base && jt <= last_j0) ? row_off + OutElem<OUT>::kBytes * jt : kOOB;
     asm volatile("" ::: "memory");
   }
-  __device__ __forceinline__ void finish() { buffer_store4_nt(r, pend_off, pend); }
+  __device__ __forceinline__ void finish() { OutElem<OUT>::store4(r, pend_off, pend); }
 };
 
 }  // namespace mqa

@@ -9,6 +9,9 @@ namespace mqa {
 // Output modes of the dense kernel.
 enum Store : int { kDenseClean = 0, kDenseKeep = 1, kCompressed = 2 };
 
+// Element type of the weights and of the logits (the C ABI's mqa_float).
+enum FloatType : int { kF32 = 0, kBF16 = 1 };
+
 // Waves per block of the paged kernel.  One: every value a wave needs to be
 // uniform (its schedule slot, its buffer resources) then comes from blockIdx
 // and the kernel arguments, which live in SGPRs already.
@@ -30,14 +33,15 @@ struct DenseParams {
   const uint8_t* kv;       // [Skv, D] bytes (fp4: D/2)
   const uint8_t* kv_sf;    // [Skv, D/32] or null
   const float* kv_scale;   // [Skv] (FP8) or null
-  const float* w;          // [Sq, H]
+  const void* w;           // [Sq, H] fp32 or bf16 (w_bf16)
   const int32_t* k_start;  // [Sq]
   const int32_t* k_end;    // [Sq]
   const int64_t* row_off;  // [Sq + 1] (compressed) or null
-  float* out;
+  void* out;               // fp32 or bf16 elements (the kernel's OUT)
   int64_t stride;          // dense row stride in elements
   int32_t sq, skv;
   int32_t n_chunks;        // chunks per 4-row group (each computes an equal run of the rows' range)
+  int32_t w_bf16;          // weights are bf16
   const uint8_t* ql;       // [Sq, 4, D] e4m3 pieces of the weighted query sum (H = 64)
   const uint8_t* ql_sf;    // [Sq, 4, D/32] their e8m0 scales
 };
@@ -49,10 +53,11 @@ constexpr int kLinHeads = 64;
 struct QsumParams {
   const uint8_t* q;        // [Sq, H, D] codes (fp4: D/2 bytes per row)
   const uint8_t* q_sf;     // [Sq, H, D/32] or null
-  const float* w;          // [Sq, H]
+  const void* w;           // [Sq, H] fp32 or bf16 (w_bf16)
   uint8_t* ql;             // [Sq, 4, D]
   uint8_t* ql_sf;          // [Sq, 4, D/32]
   int32_t sq;
+  int32_t w_bf16;
 };
 
 struct PagedParams {
@@ -61,21 +66,26 @@ struct PagedParams {
   const uint8_t* kv;         // [num_blocks, bs, D]
   const uint8_t* kv_sf;      // [num_blocks, bs, D/32]
   const float* kv_scale;     // [num_blocks, bs]
-  const float* w;            // [batch*next_n, H]
+  const void* w;             // [batch*next_n, H] fp32 or bf16 (w_bf16)
   const int32_t* ctx;        // [batch]
   const int32_t* bt;         // [batch, bt_stride]
   int64_t bt_stride;
   const int32_t* sched;      // [num_splits + 1][2]
-  float* out;
+  void* out;                 // fp32 or bf16 elements (the kernel's OUT)
   int64_t stride;
   int32_t batch, next_n, bs, num_blocks, max_ctx, num_splits, nb_max;
+  int32_t w_bf16;
 };
 
-hipError_t launch_dense(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
+hipError_t launch_dense(int fmt, int h, int d, int store, int out, const DenseParams& p,
+                        hipStream_t s);
+hipError_t launch_dense_f32(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
+hipError_t launch_dense_bf16(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
 hipError_t launch_qsum(int fmt, int d, const QsumParams& p, hipStream_t s);
 hipError_t launch_compressed_offsets(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
                                      int64_t* off, hipStream_t s);
-hipError_t launch_paged(int fmt, int h, int d, int clean, const PagedParams& p, hipStream_t s);
+hipError_t launch_paged(int fmt, int h, int d, int clean, int out, const PagedParams& p,
+                        hipStream_t s);
 hipError_t launch_paged_metadata(const int32_t* ctx, int32_t batch, int32_t bs, int32_t max_ctx,
                                  int32_t num_splits, int32_t* sched, hipStream_t s);
 

@@ -19,12 +19,14 @@
 
 namespace mqa {
 
-template <int FMT, int H, int D, bool CLEAN>
+template <int FMT, int H, int D, bool CLEAN, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
   // Decode batches are small: the weighted-query-sum launch would cost more
   // than the halved epilogue saves, so the paged kernel keeps max + fma.
   using RG = RowGroup<FMT, H, D>;
   using L = OperandLayout<FMT, D>;
+  using OE = OutElem<OUT>;
+  constexpr int kOB = OE::kBytes;              // bytes per logits element
   constexpr int kNKB = RG::kNKB;
   constexpr int kRowBytes = RG::kRowBytes;
   constexpr int kBtWindow = kWaveLanes;        // block-table entries held per lane
@@ -77,11 +79,11 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
       const bool row_ok = t0 + g < p.next_n;
       const int t_e = min(t0 + g, p.next_n - 1);
       const int t_a = min(t0 + ((lane >> 2) & 3), p.next_n - 1);
-      rg.load(p.q, p.q_sf, p.w, r0 + t_a, r0 + t_e, lane);
+      rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, r0 + t_a, r0 + t_e, lane);
       const int e_tok = clampi(ctx - p.next_n + t_e + 1, 0, len);   // this lane's row end
-      const Rsrc out_r = make_rsrc(p.out + r0 * p.stride,
-                                   (uint32_t)(p.next_n * p.stride * 4));
-      const int lane_off = (t_e * (int)p.stride + n) * 4;
+      const Rsrc out_r = make_rsrc(static_cast<char*>(p.out) + r0 * p.stride * kOB,
+                                   (uint32_t)(p.next_n * p.stride * kOB));
+      const int lane_off = (t_e * (int)p.stride + n) * kOB;
       const int rel_n = n - e_tok;           // j0 + rel_n < 0  iff  column in range
 
       for (int sub = blk; sub < seg_end; sub += kBtWindow) {
@@ -118,23 +120,23 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
           // columns 4 (l % 16) .. +3 of a trip); in range iff column < e_tok.
           const int lim = col1 & ~3;
           const int last_j0 = row_ok ? lim - 4 * n - 4 : -0x40000000;
-          StagedSink sink{stage, out_r, col0, g * kTripCols + n, g * kTripCols + 4 * n,
-                          (t_e * (int)p.stride + 4 * n) * 4, last_j0, n, e_tok, ninf4, kOOB};
+          StagedSink<OUT> sink{stage, out_r, col0, g * kTripCols + n, g * kTripCols + 4 * n,
+                               (t_e * (int)p.stride + 4 * n) * kOB, last_j0, n, e_tok, ninf4, kOOB};
           const int walked = compute_span<kFlip>(rg, col0, col1, o, load, sink);
           if ((col1 & 3) != 0) {             // max_ctx not a multiple of 4: 1..3 columns
             const int gs = col1 & ~3, jt = walked - kTripCols;
             if (row_ok && gs + n < col1) {
               float v = neg_inf();
               if (gs >= jt && gs < walked) v = sink.buffer(jt)[g * kTripCols + (gs - jt) + n];
-              buffer_store_nt(out_r, (t_e * (int)p.stride + gs + n) * 4, v);
+              OE::store1(out_r, (t_e * (int)p.stride + gs + n) * kOB, v);
             }
           }
         } else {
           auto off = [&](int j0, float& v) {
             (void)v;
-            return (j0 < wlim_n && j0 + rel_n < 0) ? lane_off + 4 * j0 : kOOB;
+            return (j0 < wlim_n && j0 + rel_n < 0) ? lane_off + kOB * j0 : kOOB;
           };
-          DwordSink<decltype(off)> sink{out_r, off, col0};
+          DwordSink<OUT, decltype(off)> sink{out_r, off, col0};
           compute_span<kFlip>(rg, col0, col1, o, load, sink);
         }
       }
@@ -150,57 +152,64 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
       const int c = (int)(f - (int64_t)fb * p.nb_max);
       const int len = clampi(p.ctx[fb], 0, p.max_ctx);
       if (c < ((len + bs - 1) >> bs_shift)) continue;
-      const Rsrc out_r = make_rsrc(p.out + (int64_t)fb * p.next_n * p.stride,
-                                   (uint32_t)(p.next_n * p.stride * 4));
+      const Rsrc out_r = make_rsrc(static_cast<char*>(p.out) + (int64_t)fb * p.next_n * p.stride * kOB,
+                                   (uint32_t)(p.next_n * p.stride * kOB));
       // 16-byte groups (lane l: row l / 16 of a 4-row group, columns
       // 4 (l % 16) .. +3), then the 1..3 columns of a last group cut by max_ctx
       const int c1 = min((c + 1) << bs_shift, p.max_ctx);
       for (int t0 = 0; t0 < p.next_n; t0 += kRowsPerWave) {
         const bool row_ok = t0 + g < p.next_n;
         const int t_e = min(t0 + g, p.next_n - 1);
-        const int grp_off = (t_e * (int)p.stride + 4 * n) * 4;
+        const int grp_off = (t_e * (int)p.stride + 4 * n) * kOB;
         for (int j0 = c << bs_shift; j0 < c1; j0 += kTripCols)
-          buffer_store4_nt(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + 4 * j0 : kOOB, ninf4);
+          OE::store4(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + kOB * j0 : kOOB, ninf4);
         if ((c1 & 3) != 0 && row_ok && (c1 & ~3) + n < c1 && (c1 & ~3) >= (c << bs_shift))
-          buffer_store_nt(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * 4, neg_inf());
+          OE::store1(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * kOB, neg_inf());
       }
     }
   }
 }
 
-template <int FMT, int H, int D>
+template <int FMT, int H, int D, int OUT>
 static hipError_t launch_paged_inst(int clean, const PagedParams& p, hipStream_t s) {
   const int grid = (p.num_splits + kWavesPerBlock - 1) / kWavesPerBlock;
   if (clean) {
-    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int FMT, int H>
+template <int FMT, int H, int OUT>
 static hipError_t paged_d(int d, int clean, const PagedParams& p, hipStream_t s) {
-  return d == 64 ? launch_paged_inst<FMT, H, 64>(clean, p, s)
-                 : launch_paged_inst<FMT, H, 128>(clean, p, s);
+  return d == 64 ? launch_paged_inst<FMT, H, 64, OUT>(clean, p, s)
+                 : launch_paged_inst<FMT, H, 128, OUT>(clean, p, s);
 }
 
-template <int FMT>
+template <int FMT, int OUT>
 static hipError_t paged_h(int h, int d, int clean, const PagedParams& p, hipStream_t s) {
   switch (h) {
-    case 8: return paged_d<FMT, 8>(d, clean, p, s);
-    case 16: return paged_d<FMT, 16>(d, clean, p, s);
-    case 32: return paged_d<FMT, 32>(d, clean, p, s);
-    default: return paged_d<FMT, 64>(d, clean, p, s);
+    case 8: return paged_d<FMT, 8, OUT>(d, clean, p, s);
+    case 16: return paged_d<FMT, 16, OUT>(d, clean, p, s);
+    case 32: return paged_d<FMT, 32, OUT>(d, clean, p, s);
+    default: return paged_d<FMT, 64, OUT>(d, clean, p, s);
   }
 }
 
-hipError_t launch_paged(int fmt, int h, int d, int clean, const PagedParams& p, hipStream_t s) {
+template <int OUT>
+static hipError_t paged_fmt(int fmt, int h, int d, int clean, const PagedParams& p, hipStream_t s) {
   switch (fmt) {
-    case kFP8: return paged_h<kFP8>(h, d, clean, p, s);
-    case kMXFP8: return paged_h<kMXFP8>(h, d, clean, p, s);
-    default: return paged_h<kMXFP4>(h, d, clean, p, s);
+    case kFP8: return paged_h<kFP8, OUT>(h, d, clean, p, s);
+    case kMXFP8: return paged_h<kMXFP8, OUT>(h, d, clean, p, s);
+    default: return paged_h<kMXFP4, OUT>(h, d, clean, p, s);
   }
+}
+
+hipError_t launch_paged(int fmt, int h, int d, int clean, int out, const PagedParams& p,
+                        hipStream_t s) {
+  return out == kBF16 ? paged_fmt<kBF16>(fmt, h, d, clean, p, s)
+                      : paged_fmt<kF32>(fmt, h, d, clean, p, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void qsum_kernel(QsumParams p) {
       code[h] = *reinterpret_cast<const uint32_t*>(p.q + hr * kRowBytes + k0);
     }
     if constexpr (FmtInfo<FMT>::kMX) sf[h] = p.q_sf[hr * kNKB + (k0 >> 5)];
-    wt[h] = p.w[hr];
+    wt[h] = p.w_bf16 ? bf16_value(static_cast<const uint16_t*>(p.w)[hr])
+                     : static_cast<const float*>(p.w)[hr];
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -36,6 +36,19 @@ def stream(seed, name):
 # encoders (input preparation only)
 # --------------------------------------------------------------------------
 
+def encode_bf16(x):
+    """float32 array -> uint16 bfloat16 bit patterns, nearest with ties to
+    even (finite inputs).  bf16 weights are an input format; the value both
+    sides see is decode_bf16 of these bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def decode_bf16(bits):
+    """uint16 bfloat16 bit patterns -> their exact float32 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def encode_e4m3(x):
     """float array -> uint8 e4m3fn codes, clipped to +-448, ties to even."""
     x = np.clip(np.asarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX)

@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported():
 def dense_args(**kw):
     a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kv_scale=FAKE, w=FAKE,
              ks=FAKE, ke=FAKE, out=FAKE, stride=64, sq=16, skv=64, h=64, d=128, clean=1,
-             stream=None)
+             w_type=0, out_type=0, stream=None)
     a.update(kw)
     return list(a.values())
 
@@ -74,6 +74,9 @@ def dense_args(**kw):
     (dict(sq=-1), INVALID),
     (dict(skv=-5), INVALID),
     (dict(stride=1 << 28), UNSUPPORTED),
+    (dict(w_type=2), INVALID),
+    (dict(out_type=-1), INVALID),
+    (dict(out_type=1, stride=65), INVALID),         # bf16 logits need an even stride
 ])
 def test_dense_validation_fails_before_any_launch(change, expect):
     assert lib.mqa_logits(*dense_args(**change)) == expect
@@ -84,17 +87,21 @@ def test_empty_problems_are_noops():
     assert lib.mqa_logits(*dense_args(sq=0)) == OK
     assert lib.mqa_logits(*dense_args(skv=0, stride=0)) == OK
     assert lib.mqa_logits_compressed(0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, 0, 64, 64, 128, None) == OK
+                                     FAKE, FAKE, 0, 64, 64, 128, 0, 0, None) == OK
 
 
 def test_compressed_validation():
-    base = [0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 64, 128, None]
+    base = [0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 64, 128, 0, 0,
+            None]
     bad = list(base)
     bad[9] = None                                   # row_offsets
     assert lib.mqa_logits_compressed(*bad) == INVALID
     bad = list(base)
     bad[13] = 40                                    # H
     assert lib.mqa_logits_compressed(*bad) == UNSUPPORTED
+    bad = list(base)
+    bad[16] = 5                                     # logits type
+    assert lib.mqa_logits_compressed(*bad) == INVALID
     assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, -1, 10, FAKE, None) == INVALID
     assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, 4, 10, None, None) == INVALID
 
@@ -126,7 +133,7 @@ def paged_args(**kw):
     a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kvs=FAKE, w=FAKE, ctx=FAKE,
              bt=FAKE, bt_stride=512, sched=FAKE, out=FAKE, stride=32768, batch=64, next_n=4,
              h=64, d=128, bs=64, num_blocks=36000, max_ctx=32768, splits=1024, clean=1,
-             stream=None)
+             w_type=0, out_type=0, stream=None)
     a.update(kw)
     return list(a.values())
 
@@ -140,6 +147,8 @@ def paged_args(**kw):
     (dict(h=24), UNSUPPORTED),
     (dict(next_n=20), UNSUPPORTED),
     (dict(kvs=None), INVALID),
+    (dict(w_type=3), INVALID),
+    (dict(out_type=1, stride=32769), INVALID),      # bf16 logits need an even stride
 ])
 def test_paged_validation(change, expect):
     assert lib.paged_mqa_logits(*paged_args(**change)) == expect
