@@ -92,6 +92,10 @@ typedef enum {
  *            [Skv, logits_stride) are never written.
  *   clean_logits != 0: entries outside a row's range are written as -inf;
  *   clean_logits == 0: they are left untouched.
+ *   schedule, num_splits: NULL (the rows' work is split into equal column
+ *            chunks), or a work schedule from mqa_logits_metadata for these
+ *            k_start, k_end, Sq, Skv and num_splits; the output is bit for bit
+ *            the same either way.
  * Sq == 0 or Skv == 0 is a no-op that returns MQA_OK.
  */
 mqa_status mqa_logits(mqa_dtype dt,
@@ -102,7 +106,29 @@ mqa_status mqa_logits(mqa_dtype dt,
                       void* logits, int64_t logits_stride,
                       int32_t sq, int32_t skv, int32_t h, int32_t d,
                       int32_t clean_logits, mqa_float weights_type, mqa_float logits_type,
-                      hipStream_t stream);
+                      const int32_t* schedule, int32_t num_splits, hipStream_t stream);
+
+/*
+ * Work schedule for mqa_logits / mqa_logits_compressed (the schedule_meta of
+ * the reproducer in "[PR #435] Improve SM100 MX MQA logits clean-output
+ * performance", made by get_mqa_logits_metadata from the ranges; Validation
+ * requires the scheduled output to equal the unscheduled one).
+ *
+ * Work units: rows are taken in groups of 4 (group g = rows 4g .. 4g+3).  With
+ * s_i, e_i the clamped ranges, a group whose rows are all empty has one unit;
+ * otherwise, with lo = min s_i and hi = max e_i over its non-empty rows, it has
+ * ceil((hi - (lo & ~63)) / 64) units (64-column trips of the union of its
+ * ranges).  The W units in group-major order are cut into num_splits
+ * contiguous pieces, piece c = units [floor(c*W/num_splits),
+ * floor((c+1)*W/num_splits)); schedule [num_splits + 1][2] int32 receives
+ * (g, t) of the first unit of each piece and (ceil(Sq/4), 0) for the end (or
+ * for a piece that starts at W).  Requires 1 <= num_splits <= 65536 and
+ * Sq <= 32768.
+ */
+int64_t mqa_logits_metadata_size(int32_t num_splits);  /* int32 count */
+mqa_status mqa_logits_metadata(const int32_t* k_start, const int32_t* k_end,
+                               int32_t sq, int32_t skv, int32_t num_splits,
+                               int32_t* schedule, hipStream_t stream);
 
 /*
  * Row offsets of the compressed layout ("Compressed Logits" in the DeepGEMM
@@ -128,6 +154,7 @@ mqa_status mqa_logits_compressed(mqa_dtype dt,
                                  const int64_t* row_offsets, void* logits_packed,
                                  int32_t sq, int32_t skv, int32_t h, int32_t d,
                                  mqa_float weights_type, mqa_float logits_type,
+                                 const int32_t* schedule, int32_t num_splits,
                                  hipStream_t stream);
 
 /*

@@ -8,6 +8,7 @@ raises.
 
 Entry points (same names as the C ABI):
   mqa_logits                      dense clean (or keep) logits
+  mqa_logits_metadata             work schedule for the dense / compressed calls
   mqa_logits_compressed_offsets   row offsets of the packed layout
   mqa_logits_compressed           packed logits
   paged_mqa_logits_metadata       paged work split
@@ -44,10 +45,12 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sigs = {
-        "mqa_logits": [I32, P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, I32, P],
+        "mqa_logits": [I32, P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, I32,
+                       P, I32, P],
+        "mqa_logits_metadata": [P, P, I32, I32, I32, P, P],
         "mqa_logits_compressed_offsets": [P, P, I32, I32, P, P],
         "mqa_logits_compressed": [I32, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
-                                  P],
+                                  P, I32, P],
         "paged_mqa_logits_metadata": [P, I32, I32, I32, I32, I32, P, P],
         "paged_mqa_logits": [I32, P, P, P, P, P, P, P, P, I64, P, P, I64,
                              I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, P],
@@ -56,8 +59,9 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = argtypes
         fn.restype = ctypes.c_int
-    lib.paged_mqa_logits_metadata_size.argtypes = [I32]
-    lib.paged_mqa_logits_metadata_size.restype = I64
+    for name in ("paged_mqa_logits_metadata_size", "mqa_logits_metadata_size"):
+        getattr(lib, name).argtypes = [I32]
+        getattr(lib, name).restype = I64
     lib.mqa_num_cus.argtypes = [I32]
     lib.mqa_num_cus.restype = I32
     lib.paged_mqa_logits_default_splits.argtypes = [I32]
@@ -69,7 +73,8 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ("mqa_logits", "mqa_logits_compressed_offsets", "mqa_logits_compressed",
+EXPORTED = ("mqa_logits", "mqa_logits_metadata_size", "mqa_logits_metadata",
+            "mqa_logits_compressed_offsets", "mqa_logits_compressed",
             "paged_mqa_logits_metadata_size", "paged_mqa_logits_metadata",
             "paged_mqa_logits", "mqa_num_cus", "paged_mqa_logits_default_splits",
             "mqa_last_error")
@@ -129,10 +134,29 @@ def paged_mqa_logits_default_splits(device=0):
     return n
 
 
+def _schedule(schedule):
+    if schedule is None:
+        return None, 0
+    return _ptr(schedule), schedule.shape[0] - 1
+
+
+def mqa_logits_metadata(k_start, k_end, skv, num_splits=None, out=None):
+    """int32 [num_splits + 1, 2] work schedule for mqa_logits /
+    mqa_logits_compressed with these ranges."""
+    if num_splits is None:
+        num_splits = paged_mqa_logits_default_splits(k_start.device.index or 0)
+    if out is None:
+        out = torch.empty(num_splits + 1, 2, dtype=torch.int32, device=k_start.device)
+    _check(lib.mqa_logits_metadata(_ptr(k_start), _ptr(k_end), k_start.shape[0], skv,
+                                   num_splits, _ptr(out), _stream(k_start)))
+    return out
+
+
 def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
-               clean_logits=True, out=None, logits_dtype=torch.float32):
+               clean_logits=True, out=None, logits_dtype=torch.float32, schedule=None):
     """Dense logits [Sq, Skv] of logits_dtype (out may be a wider-strided row
-    view; its dtype then decides).  weights: float32 or bfloat16."""
+    view; its dtype then decides).  weights: float32 or bfloat16.  schedule:
+    None or mqa_logits_metadata's result for the same ranges."""
     sq, h = weights.shape
     skv = kv.shape[0]
     if out is None:
@@ -144,7 +168,7 @@ def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
         _ptr(weights), _ptr(k_start), _ptr(k_end), ctypes.c_void_p(out.data_ptr()),
         out.stride(0) if sq > 0 else skv, sq, skv, h, _head_dim(fmt, q),
         1 if clean_logits else 0, _float_type(weights.dtype, "weights"),
-        _float_type(out.dtype, "logits"), _stream(q)))
+        _float_type(out.dtype, "logits"), *_schedule(schedule), _stream(q)))
     return out
 
 
@@ -159,7 +183,8 @@ def mqa_logits_compressed_offsets(k_start, k_end, skv, out=None):
 
 
 def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
-                          row_offsets=None, out=None, logits_dtype=torch.float32):
+                          row_offsets=None, out=None, logits_dtype=torch.float32,
+                          schedule=None):
     """Packed logits; returns (packed [total] of logits_dtype, row_offsets int64
     [Sq+1]).
 
@@ -174,7 +199,7 @@ def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv), _ptr(kv_sf), _ptr(kv_scale),
         _ptr(weights), _ptr(k_start), _ptr(k_end), _ptr(row_offsets), _ptr(out),
         sq, skv, h, _head_dim(fmt, q), _float_type(weights.dtype, "weights"),
-        _float_type(out.dtype, "logits"), _stream(q)))
+        _float_type(out.dtype, "logits"), *_schedule(schedule), _stream(q)))
     return out, row_offsets
 
 

@@ -146,12 +146,35 @@ mqa_status with_qsum(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   return hip_status(e, who);
 }
 
+// The dense work schedule (mqa_logits_metadata): 4-row groups, at most
+// kMaxSchedGroups of them (the metadata kernel's prefix lives in LDS), and a
+// unit total that fits int32.
+constexpr int64_t kMaxSchedGroups = 8192;
+
+mqa_status check_dense_schedule(int32_t sq, int32_t skv, int32_t num_splits, const char* who) {
+  if (num_splits < 1 || num_splits > 65536)
+    return fail(MQA_ERR_INVALID_ARG, "%s: num_splits=%d not in [1, 65536]", who, num_splits);
+  const int64_t groups = ((int64_t)sq + 3) / 4;
+  if (groups > kMaxSchedGroups)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: a schedule covers at most %lld rows", who,
+                (long long)(4 * kMaxSchedGroups));
+  if (groups * (((int64_t)skv + 63) / 64 + 1) >= 0x7fffffff)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: Sq x Skv too large for a schedule", who);
+  return MQA_OK;
+}
+
 mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* kv,
                      const uint8_t* kv_sf, const float* kv_scale, const void* weights,
                      mqa_float weights_type, const int32_t* k_start, const int32_t* k_end,
                      const int64_t* row_off, void* out, mqa_float logits_type, int64_t stride,
                      int32_t sq, int32_t skv, int32_t h, int32_t d, int store,
-                     hipStream_t stream, const char* who) {
+                     const int32_t* schedule, int32_t num_splits, hipStream_t stream,
+                     const char* who) {
+  if (schedule) {
+    mqa_status st = check_dense_schedule(sq, skv, num_splits, who);
+    if (st != MQA_OK) return st;
+    if (!aligned(schedule, 4)) return fail(MQA_ERR_INVALID_ARG, "%s: schedule misaligned", who);
+  }
   const int64_t row_bytes = (dt == MQA_MXFP4_E2M1 ? d / 2 : d);
   if ((int64_t)skv * row_bytes >= kMaxRangeBytes || (int64_t)skv * 16 >= kMaxRangeBytes)
     return fail(MQA_ERR_UNSUPPORTED, "%s: Skv=%d too large", who, skv);
@@ -171,8 +194,12 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   p.skv = skv;
   p.n_chunks = pick_chunks(sq, skv);
   p.w_bf16 = weights_type == MQA_BF16;
+  p.sched = schedule;
+  p.num_splits = schedule ? num_splits : 0;
   const int out_type = logits_type == MQA_BF16 ? mqa::kBF16 : mqa::kF32;
-  const int64_t grid = (int64_t)((sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves)) * p.n_chunks;
+  const int64_t grid =
+      schedule ? ((int64_t)num_splits + mqa::kDenseWaves - 1) / mqa::kDenseWaves
+               : (int64_t)((sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves)) * p.n_chunks;
   if (grid > 0x7fffffff) return fail(MQA_ERR_UNSUPPORTED, "%s: problem too large", who);
   if (debug_enabled())
     fprintf(stderr,
@@ -211,7 +238,7 @@ mqa_status mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const vo
                       const int32_t* k_start, const int32_t* k_end, void* logits,
                       int64_t logits_stride, int32_t sq, int32_t skv, int32_t h, int32_t d,
                       int32_t clean_logits, mqa_float weights_type, mqa_float logits_type,
-                      hipStream_t stream) {
+                      const int32_t* schedule, int32_t num_splits, hipStream_t stream) {
   const char* who = "mqa_logits";
   if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
   if (logits_stride < skv) return fail(MQA_ERR_INVALID_ARG, "%s: logits_stride < Skv", who);
@@ -228,7 +255,8 @@ mqa_status mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const vo
     return fail(MQA_ERR_UNSUPPORTED, "%s: logits_stride %lld too large", who, (long long)logits_stride);
   return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type, k_start, k_end,
                    nullptr, logits, logits_type, logits_stride, sq, skv, h, d,
-                   clean_logits ? mqa::kDenseClean : mqa::kDenseKeep, stream, who);
+                   clean_logits ? mqa::kDenseClean : mqa::kDenseKeep, schedule, num_splits,
+                   stream, who);
 }
 
 mqa_status mqa_logits_compressed_offsets(const int32_t* k_start, const int32_t* k_end, int32_t sq,
@@ -247,7 +275,8 @@ mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_s
                                  const int32_t* k_start, const int32_t* k_end,
                                  const int64_t* row_offsets, void* logits_packed, int32_t sq,
                                  int32_t skv, int32_t h, int32_t d, mqa_float weights_type,
-                                 mqa_float logits_type, hipStream_t stream) {
+                                 mqa_float logits_type, const int32_t* schedule,
+                                 int32_t num_splits, hipStream_t stream) {
   const char* who = "mqa_logits_compressed";
   if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
   if (sq == 0 || skv == 0) return ok();
@@ -261,7 +290,27 @@ mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_s
     return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
   return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type, k_start, k_end,
                    row_offsets, logits_packed, logits_type, 0, sq, skv, h, d, mqa::kCompressed,
-                   stream, who);
+                   schedule, num_splits, stream, who);
+}
+
+int64_t mqa_logits_metadata_size(int32_t num_splits) {
+  return num_splits < 1 ? -1 : 2 * (int64_t)(num_splits + 1);
+}
+
+mqa_status mqa_logits_metadata(const int32_t* k_start, const int32_t* k_end, int32_t sq,
+                               int32_t skv, int32_t num_splits, int32_t* schedule,
+                               hipStream_t stream) {
+  const char* who = "mqa_logits_metadata";
+  if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
+  mqa_status st = check_dense_schedule(sq, skv, num_splits, who);
+  if (st != MQA_OK) return st;
+  if (!schedule || (sq > 0 && (!k_start || !k_end)))
+    return fail(MQA_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned(schedule, 4) || !aligned(k_start, 4) || !aligned(k_end, 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  return hip_status(mqa::launch_dense_metadata(k_start, k_end, sq, skv, num_splits, schedule,
+                                               stream),
+                    who);
 }
 
 int64_t paged_mqa_logits_metadata_size(int32_t num_splits) {

@@ -1,6 +1,6 @@
-// Dense and compressed weighted MQA logits for gfx950: the kernel template
-// and its instance dispatch (instantiated per logits type in dense.hip and
-// dense_bf16.hip).
+// Dense and compressed weighted MQA logits for gfx950: the kernel templates
+// and their instance dispatch (instantiated per logits type and work split in
+// dense.hip, dense_bf16.hip, dense_sched.hip and dense_sched_bf16.hip).
 //
 //   logits[i, j] = sum_h w[i, h] * ReLU(kv_scale[j] * <q[i, h, :], kv[j, :]>)
 //
@@ -11,13 +11,14 @@
 // Architecture Components) and "[PR #435] Improve SM100 MX MQA logits
 // clean-output performance" (Description).
 //
-// Work split: a wave owns 4 consecutive query rows and one chunk of KV
-// columns, keeps the rows' Q operands and weights in registers and walks the
-// chunk 16 tokens at a time; the 4 waves of a block take 4 consecutive row
-// groups and the same chunk.  Tokens outside the
-// union of its rows' ranges are -inf fill (no MFMA); tokens inside are
-// computed and masked per row in the same store.  No second pass, no atomics:
-// each output element is written by exactly one lane.
+// Work split: a wave owns 4 consecutive query rows and a run of KV columns,
+// keeps the rows' Q operands and weights in registers and walks the run 16
+// tokens at a time.  Without a schedule, the 4 waves of a block take 4
+// consecutive row groups and the same chunk of their columns; with one, each
+// wave walks its piece of an even split of all groups' trips.  Tokens outside
+// the union of a group's row ranges are -inf fill (no MFMA); tokens inside
+// are computed and masked per row in the same store.  No second pass, no
+// atomics: each output element is written by exactly one lane.
 #pragma once
 
 #include "common.hpp"
@@ -27,31 +28,35 @@ namespace mqa {
 
 constexpr int kDenseThreads = kWaveLanes * kDenseWaves;
 
-template <int FMT, int H, int D, int STORE, int OUT>
-__global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) {
+// The part of a 4-row group's work one wave does.  The group's computed
+// range (the union of its rows' ranges, from a trip-aligned start) is
+// `trips` trips of kTripCols columns; the wave computes trips [t_a, t_b) of it
+// and writes the output columns around them: from column 0 if `first`, up to
+// Skv if `last`.  The pieces of a group partition its rows.
+struct GroupSeg {
+  int t_a, t_b;
+  bool first, last;
+};
+
+// Trips of a 4-row group's computed range: the union [lo, hi) of its
+// non-empty rows' clamped ranges, from lo rounded down to a trip boundary
+// (0 when every row is empty).  The dense work split counts these.
+__device__ __forceinline__ int group_trips(int lo, int hi) {
+  if (lo >= hi) return 0;
+  const int lo64 = lo & ~(kTripCols - 1);
+  return (hi - lo64 + kTripCols - 1) / kTripCols;
+}
+
+// One wave's piece of row group row0 / 4; seg(trips) -> GroupSeg picks it.
+template <int FMT, int H, int D, int STORE, int OUT, class SegFn>
+__device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int wave, int lane,
+                                            SegFn&& seg) {
   using RG = RowGroup<FMT, H, D, H == kLinHeads>;
   using L = OperandLayout<FMT, D>;
   using OE = OutElem<OUT>;
   constexpr int kNKB = RG::kNKB;
   constexpr int kRowBytes = RG::kRowBytes;
   constexpr int kOB = OE::kBytes;              // bytes per logits element
-
-  const int lane = threadIdx.x & (kWaveLanes - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  // Blocks are dispatched round-robin over the 8 XCDs; renumber them so each
-  // XCD gets a contiguous run of (row-group block, chunk) work and its L2
-  // keeps that run's Q rows.  Wave w of a block takes row group
-  // kDenseWaves * (block's row-group index) + w.
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int rblock = bid / p.n_chunks;
-  const int chunk = bid - rblock * p.n_chunks;
-  const int rgroup = rblock * kDenseWaves + wave;
-
-  const int row0 = rgroup * kRowsPerWave;
-  if (row0 >= p.sq) return;
 
   // ---- this wave's 4 rows ----------------------------------------------
   const int g = lane >> 4;                     // output row of this lane
@@ -93,20 +98,16 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) 
   const int s_row = g == 0 ? s_r[0] : g == 1 ? s_r[1] : g == 2 ? s_r[2] : s_r[3];
   const int e_end = g == 0 ? e_r[0] : g == 1 ? e_r[1] : g == 2 ? e_r[2] : e_r[3];
 
-  // The union, from a trip-aligned start, splits into n_chunks runs of whole
-  // trips of nearly equal length; block `chunk` computes its run [cl, ch) and
-  // owns the output columns [c0, c1) around it (from column 0 for the first
-  // chunk, up to Skv for the last), so the blocks of a row group partition
-  // the row and do the same amount of MFMA work.
-  const bool any = lo < hi;
-  const int lo64 = any ? (lo & ~(kTripCols - 1)) : 0;
-  const int trips = any ? (hi - lo64 + kTripCols - 1) / kTripCols : 0;
-  const int b0 = min(lo64 + (int)((int64_t)chunk * trips / p.n_chunks) * kTripCols, p.skv);
-  const int b1 = min(lo64 + (int)((int64_t)(chunk + 1) * trips / p.n_chunks) * kTripCols, p.skv);
-  const int c0 = chunk == 0 ? 0 : b0;
-  const int c1 = chunk == p.n_chunks - 1 ? p.skv : b1;
+  // This wave computes trips [t_a, t_b) of the union, i.e. columns [cl, ch),
+  // and owns the output columns [c0, c1) around them.
+  const int lo64 = lo < hi ? (lo & ~(kTripCols - 1)) : 0;
+  const GroupSeg sg = seg(group_trips(lo, hi));
+  const int b0 = min(lo64 + (int)min((int64_t)sg.t_a * kTripCols, (int64_t)p.skv), p.skv);
+  const int b1 = min(lo64 + (int)min((int64_t)sg.t_b * kTripCols, (int64_t)p.skv), p.skv);
+  const int c0 = sg.first ? 0 : b0;
+  const int c1 = sg.last ? p.skv : b1;
   int cl = b0, ch = min(b1, hi);
-  if (cl >= ch) { cl = c1; ch = c1; }          // nothing to compute in this chunk
+  if (cl >= ch) { cl = c1; ch = c1; }          // nothing to compute in this piece
   const int len = max(0, min(e_end, c1) - s_row);
   const int rel_n = n - s_row;                 // (j0 + rel_n) in [0, len) iff in range
 
@@ -237,48 +238,107 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) 
   }
 }
 
+// Row groups by chunks: block b (renumbered so each XCD gets a contiguous
+// run) takes chunk b % n_chunks of 4 consecutive row groups, one per wave;
+// the union of a group's ranges splits into n_chunks runs of whole trips of
+// nearly equal length, so the chunks of a group do the same MFMA work.
 template <int FMT, int H, int D, int STORE, int OUT>
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) {
+  const int lane = threadIdx.x & (kWaveLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Blocks are dispatched round-robin over the 8 XCDs; renumber them so each
+  // XCD gets a contiguous run of (row-group block, chunk) work and its L2
+  // keeps that run's Q rows.
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int rblock = bid / p.n_chunks;
+  const int chunk = bid - rblock * p.n_chunks;
+  const int row0 = (rblock * kDenseWaves + wave) * kRowsPerWave;
+  if (row0 >= p.sq) return;
+  dense_group<FMT, H, D, STORE, OUT>(p, row0, wave, lane, [&](int trips) {
+    return GroupSeg{(int)((int64_t)chunk * trips / p.n_chunks),
+                    (int)((int64_t)(chunk + 1) * trips / p.n_chunks), chunk == 0,
+                    chunk == p.n_chunks - 1};
+  });
+}
+
+// Scheduled: wave w of block b is worker kDenseWaves * b + w and walks its
+// piece of the work list (mqa_logits_metadata): row group g contributes
+// max(trips, 1) units, one trip each (an empty group's single unit is its
+// -inf fill).  Its entries schedule[worker] = (g, t) and schedule[worker + 1]
+// bound the piece.  Entries are clamped, and every iteration moves to the next
+// group, so any schedule contents stay in bounds and the loop ends.
+template <int FMT, int H, int D, int STORE, int OUT>
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_sched_kernel(DenseParams p) {
+  const int lane = threadIdx.x & (kWaveLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x * kDenseWaves + wave;
+  if (worker >= p.num_splits) return;
+  const int n_groups = (p.sq + kRowsPerWave - 1) / kRowsPerWave;
+  int grp = clampi(p.sched[2 * worker], 0, n_groups);
+  int t = max(p.sched[2 * worker + 1], 0);
+  const int eg = clampi(p.sched[2 * worker + 2], 0, n_groups);
+  const int et = max(p.sched[2 * worker + 3], 0);
+  for (; grp < n_groups && (grp < eg || (grp == eg && t < et)); ++grp, t = 0) {
+    const int t0 = t, g_cur = grp;
+    dense_group<FMT, H, D, STORE, OUT>(p, grp * kRowsPerWave, wave, lane, [&](int trips) {
+      const int units = max(trips, 1);
+      const int t1 = g_cur < eg ? units : min(units, et);
+      return GroupSeg{t0, t1, t0 == 0, t1 >= units};
+    });
+  }
+}
+
+template <int FMT, int H, int D, int STORE, int OUT, bool SCHED>
 static hipError_t launch_dense_inst(const DenseParams& p, hipStream_t stream) {
-  const int rblocks = (p.sq + kRowsPerWave * kDenseWaves - 1) / (kRowsPerWave * kDenseWaves);
-  const int64_t grid = (int64_t)rblocks * p.n_chunks;
-  hipLaunchKernelGGL((dense_kernel<FMT, H, D, STORE, OUT>), dim3((unsigned)grid),
-                     dim3(kDenseThreads), 0, stream, p);
+  if constexpr (SCHED) {
+    const int grid = (p.num_splits + kDenseWaves - 1) / kDenseWaves;
+    hipLaunchKernelGGL((dense_sched_kernel<FMT, H, D, STORE, OUT>), dim3((unsigned)grid),
+                       dim3(kDenseThreads), 0, stream, p);
+  } else {
+    const int rblocks = (p.sq + kRowsPerWave * kDenseWaves - 1) / (kRowsPerWave * kDenseWaves);
+    const int64_t grid = (int64_t)rblocks * p.n_chunks;
+    hipLaunchKernelGGL((dense_kernel<FMT, H, D, STORE, OUT>), dim3((unsigned)grid),
+                       dim3(kDenseThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
-template <int FMT, int H, int D, int OUT>
+template <int FMT, int H, int D, int OUT, bool SCHED>
 static hipError_t dispatch_store(const DenseParams& p, int store, hipStream_t s) {
   switch (store) {
-    case kDenseClean: return launch_dense_inst<FMT, H, D, kDenseClean, OUT>(p, s);
-    case kDenseKeep: return launch_dense_inst<FMT, H, D, kDenseKeep, OUT>(p, s);
-    default: return launch_dense_inst<FMT, H, D, kCompressed, OUT>(p, s);
+    case kDenseClean: return launch_dense_inst<FMT, H, D, kDenseClean, OUT, SCHED>(p, s);
+    case kDenseKeep: return launch_dense_inst<FMT, H, D, kDenseKeep, OUT, SCHED>(p, s);
+    default: return launch_dense_inst<FMT, H, D, kCompressed, OUT, SCHED>(p, s);
   }
 }
 
-template <int FMT, int H, int OUT>
+template <int FMT, int H, int OUT, bool SCHED>
 static hipError_t dispatch_d(const DenseParams& p, int d, int store, hipStream_t s) {
-  return d == 64 ? dispatch_store<FMT, H, 64, OUT>(p, store, s)
-                 : dispatch_store<FMT, H, 128, OUT>(p, store, s);
+  return d == 64 ? dispatch_store<FMT, H, 64, OUT, SCHED>(p, store, s)
+                 : dispatch_store<FMT, H, 128, OUT, SCHED>(p, store, s);
 }
 
-template <int FMT, int OUT>
+template <int FMT, int OUT, bool SCHED>
 static hipError_t dispatch_h(const DenseParams& p, int h, int d, int store, hipStream_t s) {
   switch (h) {
-    case 8: return dispatch_d<FMT, 8, OUT>(p, d, store, s);
-    case 16: return dispatch_d<FMT, 16, OUT>(p, d, store, s);
-    case 32: return dispatch_d<FMT, 32, OUT>(p, d, store, s);
-    default: return dispatch_d<FMT, 64, OUT>(p, d, store, s);
+    case 8: return dispatch_d<FMT, 8, OUT, SCHED>(p, d, store, s);
+    case 16: return dispatch_d<FMT, 16, OUT, SCHED>(p, d, store, s);
+    case 32: return dispatch_d<FMT, 32, OUT, SCHED>(p, d, store, s);
+    default: return dispatch_d<FMT, 64, OUT, SCHED>(p, d, store, s);
   }
 }
 
-// Every (format, H, D, store mode) instance with logits of type OUT.
-template <int OUT>
+// Every (format, H, D, store mode) instance with logits of type OUT, by row
+// chunks or (SCHED) by a work schedule.
+template <int OUT, bool SCHED>
 static hipError_t dispatch_fmt(int fmt, int h, int d, int store, const DenseParams& p,
                                hipStream_t s) {
   switch (fmt) {
-    case kFP8: return dispatch_h<kFP8, OUT>(p, h, d, store, s);
-    case kMXFP8: return dispatch_h<kMXFP8, OUT>(p, h, d, store, s);
-    default: return dispatch_h<kMXFP4, OUT>(p, h, d, store, s);
+    case kFP8: return dispatch_h<kFP8, OUT, SCHED>(p, h, d, store, s);
+    case kMXFP8: return dispatch_h<kMXFP8, OUT, SCHED>(p, h, d, store, s);
+    default: return dispatch_h<kMXFP4, OUT, SCHED>(p, h, d, store, s);
   }
 }
 

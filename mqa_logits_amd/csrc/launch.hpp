@@ -42,6 +42,8 @@ struct DenseParams {
   int32_t sq, skv;
   int32_t n_chunks;        // chunks per 4-row group (each computes an equal run of the rows' range)
   int32_t w_bf16;          // weights are bf16
+  const int32_t* sched;    // [num_splits + 1][2] work schedule, or null (row chunks)
+  int32_t num_splits;
   const uint8_t* ql;       // [Sq, 4, D] e4m3 pieces of the weighted query sum (H = 64)
   const uint8_t* ql_sf;    // [Sq, 4, D/32] their e8m0 scales
 };
@@ -81,6 +83,12 @@ hipError_t launch_dense(int fmt, int h, int d, int store, int out, const DensePa
                         hipStream_t s);
 hipError_t launch_dense_f32(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
 hipError_t launch_dense_bf16(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);
+hipError_t launch_dense_sched_f32(int fmt, int h, int d, int store, const DenseParams& p,
+                                  hipStream_t s);
+hipError_t launch_dense_sched_bf16(int fmt, int h, int d, int store, const DenseParams& p,
+                                   hipStream_t s);
+hipError_t launch_dense_metadata(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
+                                 int32_t num_splits, int32_t* sched, hipStream_t s);
 hipError_t launch_qsum(int fmt, int d, const QsumParams& p, hipStream_t s);
 hipError_t launch_compressed_offsets(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
                                      int64_t* off, hipStream_t s);

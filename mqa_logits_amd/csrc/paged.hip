@@ -16,6 +16,7 @@
 // units spread round-robin over the workers in the same launch.
 #include "common.hpp"
 #include "launch.hpp"
+#include "schedule.hpp"
 
 namespace mqa {
 
@@ -213,65 +214,15 @@ hipError_t launch_paged(int fmt, int h, int d, int clean, int out, const PagedPa
 }
 
 // ---------------------------------------------------------------------------
-// Metadata: prefix sum of the per-sequence unit counts, then the first unit
-// of each of the num_splits even pieces, located by binary search.
+// Metadata: sequence b has ceil(min(ctx_b, max_ctx) / bs) units.
 // ---------------------------------------------------------------------------
-constexpr int kMetaThreads = 1024;
-constexpr int kMetaMaxBatch = 8192;
-
 __global__ __launch_bounds__(kMetaThreads) void paged_metadata_kernel(
     const int32_t* __restrict__ ctx, int32_t batch, int32_t bs, int32_t max_ctx,
     int32_t num_splits, int32_t* __restrict__ sched) {
-  __shared__ int32_t prefix[kMetaMaxBatch + 1];
-  __shared__ int32_t part[kMetaThreads];
-  const int t = threadIdx.x;
-  constexpr int kPer = kMetaMaxBatch / kMetaThreads;   // sequences per thread
-  int local[kPer];
-  int sum = 0;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int b = t * kPer + k;
-    int nb = 0;
-    if (b < batch) {
-      const int len = clampi(ctx[b], 0, max_ctx);
-      nb = (len + bs - 1) / bs;
-    }
-    local[k] = nb;
-    sum += nb;
-  }
-  part[t] = sum;
-  __syncthreads();
-  for (int step = 1; step < kMetaThreads; step <<= 1) {   // inclusive scan
-    const int v = t >= step ? part[t - step] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  int run = part[t] - sum;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int b = t * kPer + k;
-    if (b <= batch) prefix[b] = run;
-    run += local[k];
-  }
-  if (t == kMetaThreads - 1 && batch == kMetaMaxBatch) prefix[batch] = part[t];
-  __syncthreads();
-  const int64_t total = prefix[batch];
-  for (int c = t; c <= num_splits; c += kMetaThreads) {
-    const int64_t u = (int64_t)c * total / num_splits;
-    int sb = batch, sblk = 0;
-    if (u < total) {
-      int lo = 0, hi = batch;              // largest b with prefix[b] <= u
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (prefix[mid] <= u) lo = mid; else hi = mid;
-      }
-      sb = lo;
-      sblk = (int)(u - prefix[lo]);
-    }
-    sched[2 * c] = sb;
-    sched[2 * c + 1] = sblk;
-  }
+  split_units(batch, num_splits, sched, [&](int b) {
+    const int len = clampi(ctx[b], 0, max_ctx);
+    return (len + bs - 1) / bs;
+  });
 }
 
 hipError_t launch_paged_metadata(const int32_t* ctx, int32_t batch, int32_t bs, int32_t max_ctx,

@@ -21,7 +21,7 @@ Sources (page titles; sections named where they are cited):
 Modules:
   codecs     exact decode of e4m3fn, e2m1 and e8m0 codes (format definitions).
   reference  dense, compressed and paged logits plus the per-entry error bound.
-  schedule   the paged work split that the metadata entry point must produce.
+  schedule   the paged and dense work splits the metadata entry points produce.
   brute      exact rational (fractions.Fraction) evaluation for tiny inputs.
 
 Every function is pinned by tests under ``tests/`` marked ``not gpu``.
@@ -38,4 +38,4 @@ from .reference import (  # noqa: F401
     paged_logits,
     gather_paged_kv,
 )
-from .schedule import paged_schedule  # noqa: F401
+from .schedule import paged_schedule, dense_schedule  # noqa: F401

@@ -1,4 +1,5 @@
-"""The paged work split that the paged metadata entry point must produce.
+"""The work splits that the metadata entry points must produce (paged decode,
+and the dense / compressed scheduled path).
 
 Test infrastructure (see the package header).
 
@@ -20,6 +21,17 @@ The split this library defines (integer work, compared bit for bit):
     schedule[num_splits] = (batch, 0).  When W == 0 every entry is (batch, 0).
 Because one unit carries all next_n rows, next_n does not change the split; it
 is taken so that both sides are called with the same arguments.
+
+The dense split ([P4] "[PR #435] Improve SM100 MX MQA logits clean-output
+performance": the reproducer's get_mqa_logits_metadata(starts, ends, ...)
+result passed as schedule_meta; Validation: scheduled and unscheduled outputs
+are equal) is defined the same way over 4-row groups:
+  * group g holds rows 4g .. 4g+3 (those below Sq); with the clamped ranges
+    [s_i, e_i), a group whose rows are all empty has 1 unit, otherwise
+    ceil((hi - 64 * floor(lo / 64)) / 64) units, lo = min s_i and hi = max e_i
+    over its non-empty rows (64-column trips of the union of its ranges);
+  * the split and the entries are as above with (g, t) for (b, blk) and
+    ceil(Sq / 4) for batch.
 """
 
 import numpy as np
@@ -31,9 +43,10 @@ def paged_units(context_lens, block_size, max_context_len):
     return (ctx + block_size - 1) // block_size
 
 
-def paged_schedule(context_lens, next_n, block_size, max_context_len, num_splits):
-    """int32 [num_splits + 1, 2] schedule as defined in the module docstring."""
-    n = paged_units(context_lens, block_size, max_context_len)
+def split_units(n, num_splits):
+    """int32 [num_splits + 1, 2]: (item, unit) of each piece's first unit for
+    items with n[b] units each, as defined in the module docstring."""
+    n = np.asarray(n, dtype=np.int64)
     batch = n.size
     prefix = np.zeros(batch + 1, dtype=np.int64)
     np.cumsum(n, out=prefix[1:])
@@ -48,3 +61,32 @@ def paged_schedule(context_lens, next_n, block_size, max_context_len, num_splits
         b = int(np.searchsorted(prefix, u, side="right") - 1)
         out[c] = (b, u - prefix[b])
     return out
+
+
+def paged_schedule(context_lens, next_n, block_size, max_context_len, num_splits):
+    """int32 [num_splits + 1, 2] paged schedule (module docstring)."""
+    return split_units(paged_units(context_lens, block_size, max_context_len), num_splits)
+
+
+def dense_units(k_start, k_end, skv):
+    """Units of each 4-row group for the dense split (module docstring)."""
+    ks = np.asarray(k_start, dtype=np.int64)
+    ke = np.asarray(k_end, dtype=np.int64)
+    s = np.clip(ks, 0, skv)
+    e = np.clip(ke, s, skv)
+    units = []
+    for g in range(0, ks.size, 4):
+        rows = [r for r in range(g, min(g + 4, ks.size)) if e[r] > s[r]]
+        if not rows:
+            units.append(1)
+            continue
+        lo = min(int(s[r]) for r in rows)
+        hi = max(int(e[r]) for r in rows)
+        start = (lo // 64) * 64
+        units.append(-(-(hi - start) // 64))
+    return np.array(units, dtype=np.int64)
+
+
+def dense_schedule(k_start, k_end, skv, num_splits):
+    """int32 [num_splits + 1, 2] dense schedule (module docstring)."""
+    return split_units(dense_units(k_start, k_end, skv), num_splits)

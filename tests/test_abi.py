@@ -22,6 +22,7 @@ lib = mq.lib
 OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
 FAKE = ctypes.c_void_p(0x100000)          # aligned, never dereferenced
 FAKE_ODD = ctypes.c_void_p(0x100004)      # 4- but not 16-byte aligned
+FAKE_2 = ctypes.c_void_p(0x100002)        # 2- but not 4-byte aligned
 
 
 def declared_functions():
@@ -50,7 +51,7 @@ def test_every_declared_symbol_is_exported():
 def dense_args(**kw):
     a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kv_scale=FAKE, w=FAKE,
              ks=FAKE, ke=FAKE, out=FAKE, stride=64, sq=16, skv=64, h=64, d=128, clean=1,
-             w_type=0, out_type=0, stream=None)
+             w_type=0, out_type=0, sched=None, splits=0, stream=None)
     a.update(kw)
     return list(a.values())
 
@@ -77,6 +78,10 @@ def dense_args(**kw):
     (dict(w_type=2), INVALID),
     (dict(out_type=-1), INVALID),
     (dict(out_type=1, stride=65), INVALID),         # bf16 logits need an even stride
+    (dict(sched=FAKE, splits=0), INVALID),
+    (dict(sched=FAKE, splits=70000), INVALID),
+    (dict(sched=FAKE_2, splits=8), INVALID),
+    (dict(sched=FAKE, splits=8, sq=40000, ks=FAKE, ke=FAKE), UNSUPPORTED),   # > 32768 rows
 ])
 def test_dense_validation_fails_before_any_launch(change, expect):
     assert lib.mqa_logits(*dense_args(**change)) == expect
@@ -87,12 +92,12 @@ def test_empty_problems_are_noops():
     assert lib.mqa_logits(*dense_args(sq=0)) == OK
     assert lib.mqa_logits(*dense_args(skv=0, stride=0)) == OK
     assert lib.mqa_logits_compressed(0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, 0, 64, 64, 128, 0, 0, None) == OK
+                                     FAKE, FAKE, 0, 64, 64, 128, 0, 0, None, 0, None) == OK
 
 
 def test_compressed_validation():
     base = [0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 64, 128, 0, 0,
-            None]
+            None, 0, None]
     bad = list(base)
     bad[9] = None                                   # row_offsets
     assert lib.mqa_logits_compressed(*bad) == INVALID
@@ -104,6 +109,20 @@ def test_compressed_validation():
     assert lib.mqa_logits_compressed(*bad) == INVALID
     assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, -1, 10, FAKE, None) == INVALID
     assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, 4, 10, None, None) == INVALID
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((FAKE, FAKE, 16, 64, 0, FAKE, None), INVALID),          # num_splits
+    ((FAKE, FAKE, 16, 64, 8, None, None), INVALID),          # schedule
+    ((None, FAKE, 16, 64, 8, FAKE, None), INVALID),          # k_start
+    ((FAKE, FAKE, -1, 64, 8, FAKE, None), INVALID),
+    ((FAKE, FAKE, 40000, 64, 8, FAKE, None), UNSUPPORTED),
+    ((FAKE, FAKE, 16, 64, 8, FAKE_2, None), INVALID),
+])
+def test_dense_metadata_validation(args, expect):
+    assert lib.mqa_logits_metadata(*args) == expect
+    assert lib.mqa_logits_metadata_size(256) == 2 * 257
+    assert lib.mqa_logits_metadata_size(0) == -1
 
 
 def paged_meta_args(**kw):
