@@ -168,11 +168,18 @@ def check_mask(out, case, rows_per_chunk=128):
             raise SystemExit(f"mask check failed in rows [{r0}, {r1})")
 
 
-def build_step(name):
-    """Returns (step_fn, info dict) with inputs resident on cuda:0."""
+def build_step(name, schedule=False, logits_dtype="fp32"):
+    """Returns (step_fn, info dict) with inputs resident on cuda:0.
+
+    schedule: dense / compressed calls follow a work schedule made by
+    mqa_logits_metadata once, outside the steps (its own time is reported as
+    metadata_ms).  logits_dtype: fp32 or bf16 logits."""
     import torch
     import mqa_logits_amd as mq
     import synth
+
+    out_dtype = {"fp32": torch.float32, "bf16": torch.bfloat16}[logits_dtype]
+    out_size = 4 if logits_dtype == "fp32" else 2
 
     idx = WORKLOADS[name]
     fmt = name.split("-")[1] if name.startswith("c4") else None
@@ -180,24 +187,41 @@ def build_step(name):
     dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
     info = dict(workload=synth.CONFIG_NAMES[idx] + (f"_{fmt}" if fmt else ""), case=case)
 
+    def dense_schedule(ks, ke):
+        if not schedule:
+            return None, {}
+        splits = mq.paged_mqa_logits_default_splits(0)
+        sched = mq.mqa_logits_metadata(ks, ke, case.skv, splits)
+
+        def metadata_ms(n=50):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                mq.mqa_logits_metadata(ks, ke, case.skv, splits, out=sched)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+        return sched, dict(extra=lambda: {"metadata_ms": metadata_ms()})
+
     if idx in (0, 1, 4):
         d = [dev(x) for x in case.args()[1:]]
         q, q_sf, kv, kv_sf, kvs, w, ks, ke = d
+        sched, extra = dense_schedule(ks, ke)
         n_out = 2 if idx == 4 else 4          # distinct output buffers, rotated
-        outs = [torch.empty(case.sq, case.skv, dtype=torch.float32, device="cuda")
-                for _ in range(n_out)]
+        outs = [mq._logits_rows(case.sq, case.skv, out_dtype, "cuda") for _ in range(n_out)]
         state = {"i": 0}
 
         def step():
             o = outs[state["i"] % n_out]
             state["i"] += 1
-            mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o)
+            mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o, schedule=sched)
         nvalid = valid_entries_dense(case)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
-                    out_bytes=4.0 * case.sq * case.skv,
+                    out_bytes=float(out_size) * case.sq * case.skv,
                     sq=case.sq, skv=case.skv, h=case.h, d=case.d, outs=outs,
                     cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
-                             format=case.fmt, layout="dense", clean_logits=True))
+                             format=case.fmt, layout="dense", clean_logits=True,
+                             logits=logits_dtype, schedule=bool(schedule)), **extra)
         # mask check before timing (the pages' reproducer checks the mask too)
         step()
         torch.cuda.synchronize()
@@ -209,7 +233,8 @@ def build_step(name):
         q, q_sf, kv, kv_sf, kvs, w, ks, ke = d
         off = mq.mqa_logits_compressed_offsets(ks, ke, case.skv)
         total = int(off[-1].item())
-        outs = [torch.empty(total, dtype=torch.float32, device="cuda") for _ in range(4)]
+        sched, extra = dense_schedule(ks, ke)
+        outs = [torch.empty(total, dtype=out_dtype, device="cuda") for _ in range(4)]
         state = {"i": 0}
 
         def step():
@@ -217,12 +242,13 @@ def build_step(name):
             state["i"] += 1
             mq.mqa_logits_compressed_offsets(ks, ke, case.skv, out=off)
             mq.mqa_logits_compressed(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke,
-                                     row_offsets=off, out=o)
+                                     row_offsets=off, out=o, schedule=sched)
         nvalid = valid_entries_dense(case)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
-                    out_bytes=4.0 * total,
+                    out_bytes=float(out_size) * total,
                     cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
-                             format=case.fmt, layout="compressed"))
+                             format=case.fmt, layout="compressed", logits=logits_dtype,
+                             schedule=bool(schedule)), **extra)
         return step, info
 
     # paged decode
@@ -233,8 +259,7 @@ def build_step(name):
     sched = mq.paged_mqa_logits_metadata(pd["ctx"], case.next_n, case.block_size,
                                          case.max_context_len, splits)
     rows = case.batch * case.next_n
-    outs = [torch.empty(rows, case.max_context_len, dtype=torch.float32, device="cuda")
-            for _ in range(4)]
+    outs = [mq._logits_rows(rows, case.max_context_len, out_dtype, "cuda") for _ in range(4)]
     state = {"i": 0}
 
     # The schedule is made once per decoding step and shared by every layer's
@@ -262,13 +287,13 @@ def build_step(name):
     n_units = int(((length + case.block_size - 1) // case.block_size).sum())
     row_bytes = case.d * (1 if case.fmt != "mxfp4" else 0.5)
     kv_bytes = n_units * case.block_size * (row_bytes + 4)
-    out_bytes = rows * case.max_context_len * 4
+    out_bytes = rows * case.max_context_len * out_size
     info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="hbm",
                 out_bytes=out_bytes, extra=lambda: {"metadata_ms": metadata_ms()},
                 bytes=kv_bytes + out_bytes + case.q.nbytes + case.weights.nbytes,
                 cfg=dict(batch=case.batch, next_n=case.next_n, heads=case.h, head_dim=case.d,
                          block_size=case.block_size, max_context_len=case.max_context_len,
-                         format=case.fmt, layout="paged", splits=splits))
+                         format=case.fmt, layout="paged", splits=splits, logits=logits_dtype))
     return step, info
 
 
@@ -307,6 +332,9 @@ def main():
     ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--schedule", action="store_true",
+                    help="dense/compressed calls follow an mqa_logits_metadata work schedule")
+    ap.add_argument("--logits-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (the reference "
                          "point that scales HBM byte counters) and exit")
@@ -327,7 +355,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n,
                           "launches": (args.warmup or 0) + args.steps}), flush=True)
         return
-    step, info = build_step(args.workload)
+    step, info = build_step(args.workload, args.schedule, args.logits_dtype)
     if args.warmup is not None:
         for _ in range(args.warmup):
             step()
@@ -360,15 +388,18 @@ def main():
 
     flops = info["flops"]
     value = flops * args.steps / wall / 1e12
+    # the committed counter summaries cover the default call (fp32 logits, no schedule)
+    default_call = not args.schedule and args.logits_dtype == "fp32"
+    traffic = measured_traffic(args.workload) if default_call else None
     if info["bound"] == "mfma":
         achieved = flops / (per_launch_ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS[info["fmt"]]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": measured_traffic(args.workload)}
+                "frac": achieved / peak, "traffic": traffic}
     else:
         achieved = info["bytes"] / (per_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
 
     peak_probe = mfma_microbench()
     cpu = None if args.no_cpu_baseline else cpu_baseline(info, args.cpu_seconds)

@@ -20,32 +20,24 @@
 
 namespace mqa {
 
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const int e = (c >> 3) & 15, m = c & 7;
-  const float v = e == 0 ? (float)m * 0x1p-9f : ldexpf(1.f + (float)m * 0.125f, e - 7);
-  return (c & 0x80) ? -v : v;
-}
-
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const int e = (c >> 1) & 3, m = c & 1;
-  const float v = e == 0 ? 0.5f * (float)m : ldexpf(1.f + 0.5f * (float)m, e - 1);
-  return (c & 8) ? -v : v;
-}
-
-// Nearest e4m3 code of x, ties to even; |x| <= 448.
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-  const uint32_t s = x < 0.f ? 0x80u : 0u;
-  const float a = fabsf(x);
-  if (a < 0x1p-6f) {                           // subnormals: multiples of 2^-9
-    const uint32_t m = (uint32_t)rintf(a * 0x1p9f);   // 8 is the smallest normal
-    return m ? (s | m) : 0u;
+// Codes -> fp32 with the gfx950 conversion instructions (exact; e4m3 is the
+// OCP e4m3fn format, e2m1 elements low nibble first):
+// four e4m3 codes of a word, or the four e2m1 codes of its low 16 bits.
+template <int FMT>
+__device__ __forceinline__ void decode4(uint32_t word, float (&v)[4]) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f a, b;
+  if constexpr (FMT == kMXFP4) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+    b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+  } else {
+    a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
   }
-  int e;
-  const float f = frexpf(a, &e);               // a = f 2^e, f in [0.5, 1)
-  uint32_t m = (uint32_t)rintf((2.f * f - 1.f) * 8.f);
-  int be = e - 1 + 7;                          // biased exponent of (1 + m/8) 2^(e-1)
-  if (m == 8) { m = 0; ++be; }
-  return s | ((uint32_t)be << 3) | m;
+  v[0] = a[0];
+  v[1] = a[1];
+  v[2] = b[0];
+  v[3] = b[1];
 }
 
 // Thread t of a row handles elements 4t .. 4t+3 (one dword of fp8 codes, two
@@ -57,7 +49,7 @@ struct QsumShape {
   static constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
 };
 
-template <int FMT, int H, int D>
+template <int FMT, int H, int D, bool WBF16>
 __global__ __launch_bounds__(256) void qsum_kernel(QsumParams p) {
   using S = QsumShape<D>;
   constexpr int kRowBytes = FMT == kMXFP4 ? D / 2 : D;
@@ -72,33 +64,35 @@ __global__ __launch_bounds__(256) void qsum_kernel(QsumParams p) {
   uint32_t code[H];
   uint32_t sf[FmtInfo<FMT>::kMX ? H : 1];
   float wt[H];
+  const uint8_t* qrow = p.q + i * H * kRowBytes;
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    const int64_t hr = i * H + h;
     if constexpr (FMT == kMXFP4) {
-      code[h] = *reinterpret_cast<const uint16_t*>(p.q + hr * kRowBytes + (k0 >> 1));
+      code[h] = *reinterpret_cast<const uint16_t*>(qrow + h * kRowBytes + (k0 >> 1));
     } else {
-      code[h] = *reinterpret_cast<const uint32_t*>(p.q + hr * kRowBytes + k0);
+      code[h] = *reinterpret_cast<const uint32_t*>(qrow + h * kRowBytes + k0);
     }
-    if constexpr (FmtInfo<FMT>::kMX) sf[h] = p.q_sf[hr * kNKB + (k0 >> 5)];
-    wt[h] = p.w_bf16 ? bf16_value(static_cast<const uint16_t*>(p.w)[hr])
-                     : static_cast<const float*>(p.w)[hr];
+    if constexpr (FmtInfo<FMT>::kMX) sf[h] = p.q_sf[(i * H + h) * kNKB + (k0 >> 5)];
+    if constexpr (WBF16) {
+      wt[h] = bf16_value(static_cast<const uint16_t*>(p.w)[i * H + h]);
+    } else {
+      wt[h] = static_cast<const float*>(p.w)[i * H + h];
+    }
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    const float wh = 0.5f * wt[h];
+    float wh = 0.5f * wt[h];
+    if constexpr (FmtInfo<FMT>::kMX) wh = ldexpf(wh, (int)sf[h] - 127);   // the block scale
+    float v[4];
+    decode4<FMT>(code[h], v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v = FMT == kMXFP4 ? e2m1_value((code[h] >> (4 * e)) & 15u)
-                              : e4m3_value((code[h] >> (8 * e)) & 255u);
-      if constexpr (FmtInfo<FMT>::kMX) v = ldexpf(v, (int)sf[h] - 127);
-      acc[e] = __builtin_fmaf(wh, v, acc[e]);
-    }
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wh, v[e], acc[e]);
   }
 
   // Four pieces: each takes the block's residual at the largest e8m0 scale
-  // that keeps every element within e4m3's range.
+  // that keeps every element within e4m3's range (|x| 2^-sc <= 448), rounded
+  // to e4m3 (nearest, ties to even: v_cvt_pk_fp8_f32).
   float r[4] = {acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
   for (int piece = 0; piece < 4; ++piece) {
@@ -111,13 +105,13 @@ __global__ __launch_bounds__(256) void qsum_kernel(QsumParams p) {
       const float f = frexpf(m, &e);           // m / 2^sc <= 448 = 0.875 * 2^9
       sc = min(max(f <= 0.875f ? e - 9 : e - 8, -127), 127);
     }
-    uint32_t word = 0;
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[0], -sc), ldexpf(r[1], -sc), 0, false);
+    const uint32_t word =
+        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[2], -sc), ldexpf(r[3], -sc), lo, true);
+    float back[4];
+    decode4<kFP8>(word, back);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t c = e4m3_rne(ldexpf(r[e], -sc));
-      r[e] -= ldexpf(e4m3_value(c), sc);
-      word |= c << (8 * e);
-    }
+    for (int e = 0; e < 4; ++e) r[e] -= ldexpf(back[e], sc);
     const int64_t pr = i * 4 + piece;
     *reinterpret_cast<uint32_t*>(p.ql + pr * D + k0) = word;
     if ((t & 7) == 0) p.ql_sf[pr * kNKB + (k0 >> 5)] = (uint8_t)(sc + 127);
@@ -128,7 +122,11 @@ template <int FMT, int D>
 static hipError_t launch_qsum_inst(const QsumParams& p, hipStream_t s) {
   using S = QsumShape<D>;
   const int blocks = (p.sq + S::kRowsPerBlock - 1) / S::kRowsPerBlock;
-  hipLaunchKernelGGL((qsum_kernel<FMT, 64, D>), dim3(blocks), dim3(256), 0, s, p);
+  if (p.w_bf16) {
+    hipLaunchKernelGGL((qsum_kernel<FMT, 64, D, true>), dim3(blocks), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((qsum_kernel<FMT, 64, D, false>), dim3(blocks), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
