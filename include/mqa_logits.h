@@ -158,6 +158,29 @@ mqa_status mqa_logits_compressed(mqa_dtype dt,
                                  hipStream_t stream);
 
 /*
+ * Top-k over logits rows: the sparse-attention indices that consume the
+ * logits ("FlashMLA" page, flash_mla_with_kvcache parameters: `indices` of
+ * shape (batch_size, seq_len_q, topk), invalid entries -1; get_mla_metadata's
+ * `topk` sparsity parameter).
+ *   logits   [Sq, logits_stride] of logits_type (the output of mqa_logits or,
+ *            with rows b*next_n + t, of paged_mqa_logits)
+ *   k_start, k_end [Sq] int32, both or neither: row i's range is
+ *            [clamp(k_start, 0, Skv), clamp(k_end, start, Skv)); without them
+ *            every row is [0, Skv)
+ *   indices  [Sq, indices_stride] int32, indices_stride >= topk
+ * Row i's candidates are the columns of its range whose logit is not -inf.
+ * indices[i, :] receives the columns of its topk largest candidates in
+ * ascending column order, then -1 up to topk when the row has fewer.  Order:
+ * larger values first, -0 below +0 (IEEE 754 total order of the bit
+ * patterns), equal values by smaller column, so the selected set is unique.
+ * Requires topk >= 1.
+ */
+mqa_status mqa_logits_topk(const void* logits, mqa_float logits_type, int64_t logits_stride,
+                           const int32_t* k_start, const int32_t* k_end,
+                           int32_t sq, int32_t skv, int32_t topk,
+                           int32_t* indices, int64_t indices_stride, hipStream_t stream);
+
+/*
  * Paged schedule ("Implementing Paged MQA Logits Computation for Decoding" in
  * the DeepGEMM MQA-logits article: a metadata call made once per decoding
  * step from context_lens, block_kv and the SM count; "[PR #314] fix: SM90

@@ -9,6 +9,7 @@ raises.
 Entry points (same names as the C ABI):
   mqa_logits                      dense clean (or keep) logits
   mqa_logits_metadata             work schedule for the dense / compressed calls
+  mqa_logits_topk                 top-k column indices of logits rows
   mqa_logits_compressed_offsets   row offsets of the packed layout
   mqa_logits_compressed           packed logits
   paged_mqa_logits_metadata       paged work split
@@ -48,6 +49,7 @@ def _load():
         "mqa_logits": [I32, P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, I32,
                        P, I32, P],
         "mqa_logits_metadata": [P, P, I32, I32, I32, P, P],
+        "mqa_logits_topk": [P, I32, I64, P, P, I32, I32, I32, P, I64, P],
         "mqa_logits_compressed_offsets": [P, P, I32, I32, P, P],
         "mqa_logits_compressed": [I32, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                   P, I32, P],
@@ -73,7 +75,7 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ("mqa_logits", "mqa_logits_metadata_size", "mqa_logits_metadata",
+EXPORTED = ("mqa_logits", "mqa_logits_metadata_size", "mqa_logits_metadata", "mqa_logits_topk",
             "mqa_logits_compressed_offsets", "mqa_logits_compressed",
             "paged_mqa_logits_metadata_size", "paged_mqa_logits_metadata",
             "paged_mqa_logits", "mqa_num_cus", "paged_mqa_logits_default_splits",
@@ -169,6 +171,22 @@ def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
         out.stride(0) if sq > 0 else skv, sq, skv, h, _head_dim(fmt, q),
         1 if clean_logits else 0, _float_type(weights.dtype, "weights"),
         _float_type(out.dtype, "logits"), *_schedule(schedule), _stream(q)))
+    return out
+
+
+def mqa_logits_topk(logits, topk, k_start=None, k_end=None, out=None):
+    """int32 [Sq, topk] columns of each row's topk largest non--inf logits in
+    [k_start, k_end) (the whole row without ranges), ascending, -1 padded."""
+    sq, skv = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    if out is None:
+        out = torch.empty(sq, topk, dtype=torch.int32, device=logits.device)
+    _check(lib.mqa_logits_topk(
+        ctypes.c_void_p(logits.data_ptr()), _float_type(logits.dtype, "logits"),
+        logits.stride(0) if sq > 0 else skv, _ptr(k_start), _ptr(k_end), sq, skv, topk,
+        ctypes.c_void_p(out.data_ptr()), out.stride(0) if sq > 0 else topk,
+        _stream(logits)))
     return out
 
 

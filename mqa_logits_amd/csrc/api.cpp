@@ -293,6 +293,32 @@ mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_s
                    schedule, num_splits, stream, who);
 }
 
+mqa_status mqa_logits_topk(const void* logits, mqa_float logits_type, int64_t logits_stride,
+                           const int32_t* k_start, const int32_t* k_end, int32_t sq,
+                           int32_t skv, int32_t topk, int32_t* indices, int64_t indices_stride,
+                           hipStream_t stream) {
+  const char* who = "mqa_logits_topk";
+  if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
+  if (topk < 1) return fail(MQA_ERR_INVALID_ARG, "%s: topk=%d < 1", who, topk);
+  if (logits_type != MQA_F32 && logits_type != MQA_BF16)
+    return fail(MQA_ERR_INVALID_ARG, "%s: unknown logits type %d", who, (int)logits_type);
+  if (logits_stride < skv) return fail(MQA_ERR_INVALID_ARG, "%s: logits_stride < Skv", who);
+  if (indices_stride < topk) return fail(MQA_ERR_INVALID_ARG, "%s: indices_stride < topk", who);
+  if ((k_start == nullptr) != (k_end == nullptr))
+    return fail(MQA_ERR_INVALID_ARG, "%s: pass both k_start and k_end or neither", who);
+  if (sq == 0) return ok();
+  if (!indices || (skv > 0 && !logits)) return fail(MQA_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned(indices, 4) || !aligned(k_start, 4) || !aligned(k_end, 4) ||
+      !aligned(logits, logits_type == MQA_BF16 ? 2 : 4))
+    return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  if ((int64_t)skv * 4 >= kMaxRangeBytes)
+    return fail(MQA_ERR_UNSUPPORTED, "%s: Skv=%d too large", who, skv);
+  mqa::TopkParams p{logits, logits_stride, k_start, k_end, sq, skv, topk, indices,
+                    indices_stride};
+  return hip_status(
+      mqa::launch_topk(logits_type == MQA_BF16 ? mqa::kBF16 : mqa::kF32, p, stream), who);
+}
+
 int64_t mqa_logits_metadata_size(int32_t num_splits) {
   return num_splits < 1 ? -1 : 2 * (int64_t)(num_splits + 1);
 }

@@ -79,6 +79,17 @@ struct PagedParams {
   int32_t w_bf16;
 };
 
+struct TopkParams {
+  const void* logits;        // [Sq, stride] fp32 or bf16
+  int64_t stride;            // elements
+  const int32_t* k_start;    // [Sq] or null (every row is [0, Skv))
+  const int32_t* k_end;      // [Sq] or null
+  int32_t sq, skv, topk;
+  int32_t* indices;          // [Sq, out_stride] int32
+  int64_t out_stride;
+};
+
+hipError_t launch_topk(int in_type, const TopkParams& p, hipStream_t s);
 hipError_t launch_dense(int fmt, int h, int d, int store, int out, const DenseParams& p,
                         hipStream_t s);
 hipError_t launch_dense_f32(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s);

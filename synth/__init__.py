@@ -20,4 +20,5 @@ from .workloads import (  # noqa: F401
     config_case,
     CONFIG_NAMES,
     sampled_rows,
+    topk_logits,
 )

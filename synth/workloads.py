@@ -274,6 +274,34 @@ def config_case(idx, fmt=None):
     raise ValueError(idx)
 
 
+def topk_logits(sq, skv, seed, ties=True, ranges=True):
+    """Synthetic logits rows for the top-k selection: N(0, 1) values (on a
+    1/16 grid when `ties`, so equal values are common), about 5% -inf and 2%
+    signed zeros inside the rows, -inf outside the ranges.  Returns
+    (logits float32 [Sq, Skv], k_start, k_end) with the ranges None when
+    `ranges` is false; ranges mix full, empty, short and shifted rows."""
+    rng = np.random.default_rng([int(seed), 9])
+    x = rng.standard_normal((sq, skv))
+    if ties:
+        x = np.round(x * 16) / 16
+    x[rng.random((sq, skv)) < 0.05] = -np.inf
+    z = rng.random((sq, skv)) < 0.02
+    x[z] = np.where(rng.random(int(z.sum())) < 0.5, 0.0, -0.0)
+    x = x.astype(np.float32)
+    if not ranges:
+        return x, None, None
+    ks = rng.integers(-10, skv, sq)
+    ke = ks + rng.integers(-20, skv + 20, sq)
+    if sq >= 4:
+        ks[:4] = [0, 5, skv // 2, 0]
+        ke[:4] = [skv, 5, skv // 2 + 3, skv + 100]      # full, empty, short, past the end
+    cols = np.arange(skv)[None, :]
+    s = np.clip(ks, 0, skv)[:, None]
+    e = np.clip(ke, np.clip(ks, 0, skv), skv)[:, None]
+    x[(cols < s) | (cols >= e)] = -np.inf
+    return x, ks.astype(np.int32), ke.astype(np.int32)
+
+
 def sampled_rows(seed, sq, n):
     """n distinct rows in [0, Sq), always including 0 and Sq-1, sorted."""
     if n >= sq:

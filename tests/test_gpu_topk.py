@@ -1,0 +1,96 @@
+"""GPU parity of the top-k selection over logits rows (mqa_logits_topk).
+
+On synthetic logits (ties, signed zeros, -inf holes, ranges that are full,
+empty, short or past the end) the device indices must equal the oracle's bit
+for bit.  After the logits kernel, the selection is checked for validity
+against the oracle's float64 logits within their error bound (the device
+logits are not an oracle input)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_helpers import dense_on_device, dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mqa_logits_amd  # noqa: F401
+
+
+@pytest.mark.parametrize("sq,skv,topk,ranges,seed", [
+    (40, 1000, 64, True, 1),
+    (24, 32773, 2048, True, 2),
+    (16, 5000, 1, True, 3),
+    (33, 3000, 4096, False, 4),             # more than most rows hold
+    (8, 65536, 2048, False, 5),
+    (3, 1, 7, True, 6),
+])
+def test_topk_matches_oracle(sq, skv, topk, ranges, seed):
+    import mqa_logits_amd as mq
+    x, ks, ke = synth.topk_logits(sq, skv, seed, ranges=ranges)
+    log(f"[topk] fp32 Sq={sq} Skv={skv} topk={topk} ranges={ranges}")
+    got = mq.mqa_logits_topk(dev(x), topk, dev(ks), dev(ke))
+    torch.cuda.synchronize()
+    want = oracle.topk_indices(x, topk, ks, ke)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_topk_bf16_logits_and_guard_columns():
+    import mqa_logits_amd as mq
+    sq, skv, topk = 20, 7001, 300
+    x, ks, ke = synth.topk_logits(sq, skv, 11, ties=False)
+    bits = synth.encode_bf16(x)
+    xb = synth.decode_bf16(bits).reshape(x.shape)
+    buf = torch.full((sq, topk + 5), 12345, dtype=torch.int32, device="cuda")
+    log("[topk] bf16 logits, wide indices rows")
+    mq.mqa_logits_topk(dev(bits.view(np.int16)).view(torch.bfloat16), topk, dev(ks), dev(ke),
+                       out=buf[:, :topk])
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:, topk:] == 12345)
+    assert np.array_equal(b[:, :topk], oracle.topk_indices(xb, topk, ks, ke))
+
+
+def test_topk_all_equal_and_all_neg_inf_rows():
+    import mqa_logits_amd as mq
+    x = np.zeros((3, 40000), np.float32)
+    x[1] = 1.5
+    x[2] = -np.inf
+    log("[topk] all-equal rows")
+    got = mq.mqa_logits_topk(dev(x), 2048).cpu().numpy()
+    assert np.array_equal(got, oracle.topk_indices(x, 2048))
+    assert got[0].tolist() == list(range(2048)) and np.all(got[2] == -1)
+
+
+def test_topk_after_dense_logits_is_a_valid_selection():
+    import mqa_logits_amd as mq
+    sq, skv, topk = 48, 4096, 512
+    ks = np.zeros(sq, np.int64)
+    ke = skv - sq + np.arange(sq) + 1 - 3000 * (np.arange(sq) % 5 == 0)   # some short rows
+    case = synth.dense_case(sq, skv, 64, 128, "fp8", seed=77, k_start=ks, k_end=ke)
+    d = dense_on_device(case)
+    log("[topk] after mqa_logits")
+    logits = mq.mqa_logits(d["fmt"], d["q"], d["q_sf"], d["kv"], d["kv_sf"], d["kv_scale"],
+                           d["weights"], d["k_start"], d["k_end"])
+    idx = mq.mqa_logits_topk(logits, topk, d["k_start"], d["k_end"]).cpu().numpy()
+    ref, bound = oracle.dense_logits(*case.args())
+    s, e = oracle.row_ranges(case.k_start, case.k_end, skv)
+    for i in range(sq):
+        n = int(e[i] - s[i])
+        row = idx[i]
+        sel = row[row >= 0]
+        assert sel.size == min(topk, n) and np.all(row[sel.size:] == -1)
+        assert np.all(np.diff(sel) > 0) and (sel.size == 0 or (sel[0] >= s[i] and sel[-1] < e[i]))
+        if n > topk:
+            rest = np.setdiff1d(np.arange(s[i], e[i]), sel)
+            # every selected true value is at least every unselected one, up to both bounds
+            lo = (ref[i, sel] + bound[i, sel]).min()
+            hi = (ref[i, rest] - bound[i, rest]).max()
+            assert hi <= lo, f"row {i}: unselected {hi} above selected {lo}"
