@@ -216,6 +216,8 @@ def build_step(name, schedule=False, logits_dtype="fp32"):
             state["i"] += 1
             mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o, schedule=sched)
         nvalid = valid_entries_dense(case)
+        info["topk"] = lambda k: time_topk(lambda: mq.mqa_logits_topk(outs[0], k, ks, ke),
+                                           nvalid * out_size + case.sq * k * 4)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
                     out_bytes=float(out_size) * case.sq * case.skv,
                     sq=case.sq, skv=case.skv, h=case.h, d=case.d, outs=outs,
@@ -288,6 +290,9 @@ def build_step(name, schedule=False, logits_dtype="fp32"):
     row_bytes = case.d * (1 if case.fmt != "mxfp4" else 0.5)
     kv_bytes = n_units * case.block_size * (row_bytes + 4)
     out_bytes = rows * case.max_context_len * out_size
+    # top-k over whole rows: the -inf past each row's range is not a candidate
+    info["topk"] = lambda k: time_topk(lambda: mq.mqa_logits_topk(outs[0], k),
+                                       out_bytes + rows * k * 4)
     info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="hbm",
                 out_bytes=out_bytes, extra=lambda: {"metadata_ms": metadata_ms()},
                 bytes=kv_bytes + out_bytes + case.q.nbytes + case.weights.nbytes,
@@ -295,6 +300,24 @@ def build_step(name, schedule=False, logits_dtype="fp32"):
                          block_size=case.block_size, max_context_len=case.max_context_len,
                          format=case.fmt, layout="paged", splits=splits, logits=logits_dtype))
     return step, info
+
+
+def time_topk(fn, nbytes, n=50):
+    """Average time of the top-k selection over a step's logits (HIP events
+    around n back-to-back calls) and the rate of its algorithmic bytes
+    (logits read once + indices written)."""
+    import torch
+    for _ in range(5):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    return {"ms": ms, "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
 def cpu_baseline(info, seconds):
@@ -335,6 +358,8 @@ def main():
     ap.add_argument("--schedule", action="store_true",
                     help="dense/compressed calls follow an mqa_logits_metadata work schedule")
     ap.add_argument("--logits-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--topk", type=int, default=0, metavar="K",
+                    help="also time mqa_logits_topk(K) over a step's logits (reported apart)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (the reference "
                          "point that scales HBM byte counters) and exit")
@@ -419,6 +444,8 @@ def main():
     }
     if "extra" in info:
         line.update(info["extra"]())
+    if args.topk and "topk" in info:
+        line["topk"] = {"k": args.topk, **info["topk"](args.topk)}
     print(json.dumps(line), flush=True)
 
 

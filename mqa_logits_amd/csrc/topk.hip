@@ -9,11 +9,19 @@
 // order and padded with -1 when a row has fewer than topk candidates.
 //
 // One block of 1024 threads per row.  Logits map to order-preserving 32-bit
-// keys (sign-magnitude to two's-complement order), and a three-level radix
-// select (11 + 11 + 10 bits, one LDS histogram per level, each level a pass
-// over the row) finds the k-th largest key K and how many equal keys to keep.
-// A last pass writes the selected columns in column order with a block-wide
-// prefix count of (keys > K, keys == K).
+// keys (sign-magnitude to two's-complement order) and a radix select over
+// them (11 + 11 + 10 bits, one LDS histogram per level) finds the topk-th
+// largest key K and how many keys equal to K to keep.
+//   * A first pass over the row builds the top-11-bit histogram: the bin B of
+//     the topk-th key, the count above it and the count in it.
+//   * When both counts fit in LDS (the usual case) a second pass copies, in
+//     column order, the columns above B and the (key, column) pairs in B to
+//     LDS; the last two levels, the choice of B's keys and the merge of the
+//     two column-ordered lists into the output run in LDS.  Two passes over
+//     the row in all.
+//   * Otherwise every level is a pass over the row, and a last pass writes
+//     the selected columns in column order with a block-wide prefix count of
+//     (keys > K, keys == K).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,6 +50,25 @@ struct TopkRow {
       bits = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (s + c), 0, 0);
     }
     return order_key(bits);
+  }
+  // Keys of columns s + c .. s + c + 3 (one 8- or 16-byte load); columns at or
+  // past n (the range end, relative) are -inf.
+  __device__ __forceinline__ void key4(int c, int n, uint32_t (&k)[4]) const {
+    uint32_t bits[4];
+    if constexpr (IN == kBF16) {
+      typedef int v2i __attribute__((ext_vector_type(2)));
+      const v2i w = __builtin_amdgcn_raw_buffer_load_b64(r, 2 * (s + c), 0, 0);
+      bits[0] = (uint32_t)w[0] << 16;
+      bits[1] = (uint32_t)w[0] & 0xffff0000u;
+      bits[2] = (uint32_t)w[1] << 16;
+      bits[3] = (uint32_t)w[1] & 0xffff0000u;
+    } else {
+      typedef int v4i __attribute__((ext_vector_type(4)));
+      const v4i w = __builtin_amdgcn_raw_buffer_load_b128(r, 4 * (s + c), 0, 0);
+      for (int u = 0; u < 4; ++u) bits[u] = (uint32_t)w[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = c + u < n ? order_key(bits[u]) : kKeyNegInf;
   }
 };
 
@@ -75,12 +102,36 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* wave_sums, T* total) {
   return before + x - v;
 }
 
+constexpr int kTopkCap = 4 * kTopkThreads;   // LDS list capacity of the two-pass path
+
+
+// 2048 bins and a spare slot; the stride puts a bin's four copies in four
+// different LDS banks (2064 = 16 mod 64)
+constexpr int kHistStride = 2048 + 16;
+
 struct TopkShared {
-  uint32_t hist[2048];
+  uint32_t hist[kHistStride];
   uint64_t wave_sums64[kTopkWaves];
   uint32_t wave_sums32[kTopkWaves];
   uint32_t sel_bin, sel_above;
 };
+
+// The streaming kernel's column lists.
+struct TopkLists {
+  int32_t d_col[kTopkCap];    // columns above the first-level bin, in column order
+  uint32_t b_key[kTopkCap];   // keys in that bin (column order), then the chosen columns
+  int32_t b_col[kTopkCap];
+};
+
+// Elements of the ascending list a[0, n) below x.
+__device__ __forceinline__ int count_below(const int32_t* a, int n, int32_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
 
 // One radix level over the histogram in sh.hist (nbins = 2048 or 1024, in
 // descending bin order): the bin holding the need-th largest key and the
@@ -105,8 +156,9 @@ __device__ __forceinline__ void find_bin(TopkShared& sh, int nbins, uint32_t nee
 }
 
 template <int IN>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+__global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p) {
   __shared__ TopkShared sh;
+  __shared__ TopkLists ls;
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
   int s = 0, e = p.skv;
@@ -121,15 +173,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
                         s};
   int32_t* out = p.indices + row * p.out_stride;
 
-  // ---- three radix levels: K = the topk-th largest candidate key ----------
+  // ---- first level over the row: histogram of the top 11 bits -------------
   constexpr int kShift[3] = {21, 10, 0};
   constexpr int kBins[3] = {2048, 2048, 1024};
-  uint32_t need = (uint32_t)p.topk;         // keys still to place at or below the prefix
-  uint32_t prefix = 0, mask = 0;
-  uint32_t n_cand = 0;
-  bool take_all = false;
-#pragma unroll
-  for (int lvl = 0; lvl < 3; ++lvl) {
+  auto histogram_pass = [&](int lvl, uint32_t prefix, uint32_t mask) {
     for (int b = t; b < kBins[lvl]; b += kTopkThreads) sh.hist[b] = 0;
     __syncthreads();
     // four loads in flight per thread before their histogram updates
@@ -144,20 +191,141 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
           atomicAdd(&sh.hist[(k[u] >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
     }
     __syncthreads();
-    if (lvl == 0) {
-      uint32_t local = 0;
-      for (int b = t; b < 2048; b += kTopkThreads) local += sh.hist[b];
-      block_exclusive_scan<uint32_t>(local, sh.wave_sums32, &n_cand);
-      if (n_cand <= (uint32_t)p.topk) {     // every candidate is selected
-        take_all = true;
-        break;
+  };
+  histogram_pass(0, 0u, 0u);
+  uint32_t n_cand;
+  {
+    uint32_t local = 0;
+    for (int b = t; b < 2048; b += kTopkThreads) local += sh.hist[b];
+    block_exclusive_scan<uint32_t>(local, sh.wave_sums32, &n_cand);
+  }
+  const bool take_all = n_cand <= (uint32_t)p.topk;     // every candidate is selected
+  uint32_t need = (uint32_t)p.topk;         // keys still to place at or below the prefix
+  uint32_t prefix = 0, mask = 0;
+  uint32_t n_above = 0, n_bin = 0;
+  if (!take_all) {
+    find_bin(sh, 2048, need);
+    const uint32_t b1 = sh.sel_bin;
+    n_above = sh.sel_above;
+    n_bin = sh.hist[b1];
+    need -= n_above;
+    prefix = b1 << kShift[0];
+    mask = 2047u << kShift[0];
+    __syncthreads();                        // sel_* and hist read by all
+  }
+
+  if (!take_all && n_above <= (uint32_t)kTopkCap && n_bin <= (uint32_t)kTopkCap) {
+    // ---- second pass: the columns above the bin and the bin's (key, column)
+    // pairs, both in column order, into LDS ----------------------------------
+    constexpr int kTile = 4 * kTopkThreads;
+    uint64_t carry = 0;                     // (in bin << 32) | above, before the tile
+    for (int c0 = 0; c0 < n; c0 += kTile) {
+      const int c = c0 + 4 * t;
+      uint32_t kk[4];
+      uint32_t na = 0, nb = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kk[u] = c + u < n ? src.key(c + u) : kKeyNegInf;
+        const bool valid = kk[u] != kKeyNegInf;
+        na += (valid && (kk[u] & mask) > prefix) ? 1u : 0u;
+        nb += (valid && (kk[u] & mask) == prefix) ? 1u : 0u;
+      }
+      uint64_t tile_total;
+      const uint64_t before = carry + block_exclusive_scan<uint64_t>(((uint64_t)nb << 32) | na,
+                                                                     sh.wave_sums64, &tile_total);
+      uint32_t ab = (uint32_t)before, bb = (uint32_t)(before >> 32);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool valid = kk[u] != kKeyNegInf;
+        if (valid && (kk[u] & mask) > prefix) {
+          if (ab < (uint32_t)kTopkCap) ls.d_col[ab] = s + c + u;
+          ++ab;
+        } else if (valid && (kk[u] & mask) == prefix) {
+          if (bb < (uint32_t)kTopkCap) {
+            ls.b_key[bb] = kk[u];
+            ls.b_col[bb] = s + c + u;
+          }
+          ++bb;
+        }
+      }
+      carry += tile_total;
+    }
+    __syncthreads();
+    const int n_d = (int)n_above, n_b = (int)n_bin;
+
+    // ---- levels 2 and 3 over the bin's keys in LDS --------------------------
+#pragma unroll
+    for (int lvl = 1; lvl < 3; ++lvl) {
+      for (int b = t; b < kBins[lvl]; b += kTopkThreads) sh.hist[b] = 0;
+      __syncthreads();
+      for (int i = t; i < n_b; i += kTopkThreads) {
+        const uint32_t k = ls.b_key[i];
+        if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin(sh, kBins[lvl], need);
+      need -= sh.sel_above;
+      prefix |= sh.sel_bin << kShift[lvl];
+      mask |= (uint32_t)(kBins[lvl] - 1) << kShift[lvl];
+      __syncthreads();
+    }
+    const uint32_t K = prefix, need_eq = need;
+
+    // ---- the bin's chosen columns, in column order, over its keys -----------
+    uint32_t kk[4];
+    int32_t cc[4];
+    uint32_t g = 0, q = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * t + u;
+      kk[u] = i < n_b ? ls.b_key[i] : 0u;
+      cc[u] = i < n_b ? ls.b_col[i] : 0;
+      g += (i < n_b && kk[u] > K) ? 1u : 0u;
+      q += (i < n_b && kk[u] == K) ? 1u : 0u;
+    }
+    uint64_t total;
+    const uint64_t before =
+        block_exclusive_scan<uint64_t>(((uint64_t)q << 32) | g, sh.wave_sums64, &total);
+    int32_t* chosen = reinterpret_cast<int32_t*>(ls.b_key);   // every key is in registers now
+    const int n_c = (int)(p.topk - n_above);
+    uint32_t gb = (uint32_t)before, qb = (uint32_t)(before >> 32);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * t + u;
+      if (i < n_b && kk[u] > K) {
+        const uint32_t pos = gb + min(qb, need_eq);
+        if (pos < (uint32_t)kTopkCap) chosen[pos] = cc[u];
+        ++gb;
+      } else if (i < n_b && kk[u] == K) {
+        if (qb < need_eq && gb + qb < (uint32_t)kTopkCap) chosen[gb + qb] = cc[u];
+        ++qb;
       }
     }
-    find_bin(sh, kBins[lvl], need);
-    need -= sh.sel_above;
-    prefix |= sh.sel_bin << kShift[lvl];
-    mask |= (uint32_t)(kBins[lvl] - 1) << kShift[lvl];
-    __syncthreads();                          // sel_* read by all before the next level
+    __syncthreads();
+
+    // ---- merge the two ascending lists into the row's indices ----------------
+    for (int i = t; i < n_d; i += kTopkThreads) {
+      const int pos = i + count_below(chosen, n_c, ls.d_col[i]);
+      if (pos < p.topk) out[pos] = ls.d_col[i];
+    }
+    for (int j = t; j < n_c; j += kTopkThreads) {
+      const int pos = j + count_below(ls.d_col, n_d, chosen[j]);
+      if (pos < p.topk) out[pos] = chosen[j];
+    }
+    return;
+  }
+
+  // ---- otherwise: levels 2 and 3 as passes over the row ---------------------
+  if (!take_all) {
+#pragma unroll
+    for (int lvl = 1; lvl < 3; ++lvl) {
+      histogram_pass(lvl, prefix, mask);
+      find_bin(sh, kBins[lvl], need);
+      need -= sh.sel_above;
+      prefix |= sh.sel_bin << kShift[lvl];
+      mask |= (uint32_t)(kBins[lvl] - 1) << kShift[lvl];
+      __syncthreads();                      // sel_* read by all before the next level
+    }
   }
   // selected: key > K, and the first `need` keys equal to K in column order
   const uint32_t K = take_all ? 0u : prefix;
@@ -202,14 +370,227 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   for (int pos = (int)n_sel + t; pos < p.topk; pos += kTopkThreads) out[pos] = -1;
 }
 
-hipError_t launch_topk(int in_type, const TopkParams& p, hipStream_t s) {
-  if (p.sq == 0) return hipSuccess;
-  if (in_type == kBF16) {
-    hipLaunchKernelGGL(topk_kernel<kBF16>, dim3((unsigned)p.sq), dim3(kTopkThreads), 0, s, p);
+// Rows of up to kTopkThreads * R columns: the row is read once, into
+// registers (thread t holds columns 4t .. 4t+3 of every 4096-column tile, so
+// the loads coalesce), and every level and the ordered write work from there.
+// After the first level the keys in its bin are gathered (in any order) into
+// LDS and the finer levels histogram that short list.  The selection is then
+// marked in LDS bitmaps over the columns, which give column order directly.
+// Up to 32 keys per thread: at most 64 VGPRs, so two blocks (8 waves per
+// SIMD) share a compute unit and one block's loads overlap the other's work.
+template <int IN, int R>
+__global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel(TopkParams p) {
+  static_assert(R % 4 == 0 && R <= 64, "whole 4-column groups; the flag words hold 64");
+  constexpr int kTiles = R / 4;
+  constexpr int kTile = 4 * kTopkThreads;
+  __shared__ TopkShared sh;
+  constexpr int kWords = kTiles * kTile / 32;  // 32-column words of the register-held row
+  __shared__ union {
+    uint32_t hist_more[3 * kHistStride];      // copies 1..3 of the first-level histogram
+    uint32_t maps[2 * kWords];                // then the column bitmaps (key > K, key == K)
+  } u_;
+  uint32_t* const hist_more = u_.hist_more;
+  uint32_t* const gmap = u_.maps;
+  uint32_t* const qmap = u_.maps + kWords;
+  __shared__ uint32_t bin_keys[kTopkCap];     // the first-level bin's keys
+  __shared__ uint32_t bin_count;
+  const int t = threadIdx.x;
+  const int lane = t & (kWaveLanes - 1);
+  const int64_t row = blockIdx.x;
+  int s = 0, e = p.skv;
+  if (p.k_start) {
+    s = clampi(p.k_start[row], 0, p.skv);
+    e = clampi(p.k_end[row], s, p.skv);
+  }
+  const int n = e - s;                        // <= kTopkThreads * R (host dispatch)
+  constexpr int kIB = IN == kBF16 ? 2 : 4;
+  const TopkRow<IN> src{make_rsrc(static_cast<const char*>(p.logits) + row * p.stride * kIB,
+                                  (uint32_t)(p.skv * kIB)),
+                        s};
+  int32_t* out = p.indices + row * p.out_stride;
+
+  uint32_t k[kTiles][4];
+#pragma unroll
+  for (int m = 0; m < kTiles; ++m) src.key4(m * kTile + 4 * t, n, k[m]);
+
+  // ---- first level: every key, no branch; -inf counts into a spare slot ----
+  // Each quarter of a wave counts into its own copy of the histogram (most
+  // keys fall in a few bins), folded before the search.
+  const int copy = lane >> 4;
+  for (int b = t; b < kHistStride; b += kTopkThreads) sh.hist[b] = 0;
+  for (int b = t; b < 3 * kHistStride; b += kTopkThreads) hist_more[b] = 0;
+  if (t == 0) bin_count = 0;
+  __syncthreads();
+  {
+    uint32_t* h = copy > 0 ? hist_more + (copy - 1) * kHistStride : sh.hist;
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        atomicAdd(&h[k[m][u] != kKeyNegInf ? (k[m][u] >> 21) : 2048u], 1u);
+  }
+  __syncthreads();
+  uint32_t n_cand;
+  {
+    uint32_t local = 0;
+    for (int b = t; b < 2048; b += kTopkThreads) {
+      const uint32_t c = sh.hist[b] + hist_more[b] + hist_more[kHistStride + b] +
+                         hist_more[2 * kHistStride + b];
+      local += c;
+      sh.hist[b] = c;                         // copy 0 becomes the folded histogram
+    }
+    block_exclusive_scan<uint32_t>(local, sh.wave_sums32, &n_cand);
+  }
+
+  // keys > K are taken, then the first need_eq keys equal to K in column order
+  uint32_t K = 0, need_eq = 0;
+  const bool take_all = n_cand <= (uint32_t)p.topk;
+  if (!take_all) {
+    uint32_t need = (uint32_t)p.topk;
+    find_bin(sh, 2048, need);
+    const uint32_t in_bin = sh.hist[sh.sel_bin];
+    need -= sh.sel_above;
+    uint32_t prefix = sh.sel_bin << 21, mask = 2047u << 21;
+    __syncthreads();
+    bool whole_bin = in_bin == need && prefix != 0;
+    if (!whole_bin) {
+      const bool listed = in_bin <= (uint32_t)kTopkCap;
+      if (listed) {                           // gather the bin's keys
+#pragma unroll
+        for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (k[m][u] != kKeyNegInf && (k[m][u] & mask) == prefix) {
+              const uint32_t slot = atomicAdd(&bin_count, 1u);
+              if (slot < (uint32_t)kTopkCap) bin_keys[slot] = k[m][u];
+            }
+        __syncthreads();
+      }
+      constexpr int kShift[3] = {21, 10, 0};
+      constexpr int kBins[3] = {2048, 2048, 1024};
+#pragma unroll
+      for (int lvl = 1; lvl < 3; ++lvl) {
+        for (int b = t; b < kBins[lvl]; b += kTopkThreads) sh.hist[b] = 0;
+        __syncthreads();
+        if (listed) {
+          for (int i = t; i < (int)in_bin; i += kTopkThreads) {
+            const uint32_t key = bin_keys[i];
+            if ((key & mask) == prefix)
+              atomicAdd(&sh.hist[(key >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (k[m][u] != kKeyNegInf && (k[m][u] & mask) == prefix)
+                atomicAdd(&sh.hist[(k[m][u] >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin(sh, kBins[lvl], need);
+        need -= sh.sel_above;
+        const uint32_t c = sh.hist[sh.sel_bin];
+        prefix |= sh.sel_bin << kShift[lvl];
+        mask |= (uint32_t)(kBins[lvl] - 1) << kShift[lvl];
+        __syncthreads();
+        if (c == need && lvl == 1 && prefix != 0) {   // the whole finer bin is taken
+          whole_bin = true;
+          break;
+        }
+      }
+    }
+    K = whole_bin ? prefix - 1u : prefix;
+    need_eq = whole_bin ? 0u : need;
+  }
+  const uint32_t n_sel = take_all ? n_cand : (uint32_t)p.topk;
+
+  // ---- ordered write ---------------------------------------------------------
+  // Bitmaps over the row's columns: gmap (key > K) and qmap (key == K).  The
+  // block then walks them one 32-column word at a time in column order: a
+  // scan of the words' counts gives each word's first output slot and how
+  // many of its == K columns are still taken (the first need_eq in column
+  // order); each word's columns are written in ascending order.
+  for (int w = t; w < 2 * kWords; w += kTopkThreads) u_.maps[w] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < kTiles; ++m) {
+    uint32_t ng = 0, nq = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = k[m][u] != kKeyNegInf;
+      ng |= (valid && k[m][u] > K) ? 1u << u : 0u;
+      nq |= (valid && k[m][u] == K) ? 1u << u : 0u;
+    }
+    const int c = m * kTile + 4 * t;          // the 4 columns' word and bit
+    if (ng) atomicOr(&gmap[c >> 5], ng << (c & 31));
+    if (nq) atomicOr(&qmap[c >> 5], nq << (c & 31));
+  }
+  __syncthreads();
+  constexpr int kWpt = (kWords + kTopkThreads - 1) / kTopkThreads;   // per thread
+  uint32_t wg[kWpt], wq[kWpt];
+  uint32_t cg = 0, cq = 0;
+#pragma unroll
+  for (int j = 0; j < kWpt; ++j) {
+    const int w = t * kWpt + j;
+    wg[j] = w < kWords ? gmap[w] : 0u;
+    wq[j] = w < kWords ? qmap[w] : 0u;
+    cg += __popc(wg[j]);
+    cq += __popc(wq[j]);
+  }
+  uint64_t total;
+  const uint64_t before =
+      block_exclusive_scan<uint64_t>(((uint64_t)cq << 32) | cg, sh.wave_sums64, &total);
+  uint32_t gb = (uint32_t)before, qb = (uint32_t)(before >> 32);
+#pragma unroll
+  for (int j = 0; j < kWpt; ++j) {
+    // the == K columns of this word still taken: the lowest `take` set bits
+    const uint32_t nq = __popc(wq[j]);
+    uint32_t take = qb < need_eq ? min(need_eq - qb, nq) : 0u;
+    uint32_t sel_q = 0, rest = wq[j];
+    for (; take > 0; --take) {
+      const uint32_t low = rest & (0u - rest);
+      sel_q |= low;
+      rest ^= low;
+    }
+    uint32_t word = wg[j] | sel_q;
+    // == K columns placed before this word: at most need_eq (kept opaque:
+    // LLVM has been seen to drop this min here)
+    uint32_t eq_cap = need_eq;
+    asm volatile("" : "+v"(eq_cap));
+    uint32_t pos = gb + (qb < eq_cap ? qb : eq_cap);
+    const int col0 = s + 32 * (t * kWpt + j);
+    while (word) {
+      const int b = __builtin_ctz(word);
+      word &= word - 1;
+      if (pos < (uint32_t)p.topk) out[pos] = col0 + b;
+      ++pos;
+    }
+    gb += __popc(wg[j]);
+    qb += nq;
+  }
+  for (int pos = (int)n_sel + t; pos < p.topk; pos += kTopkThreads) out[pos] = -1;
+}
+
+template <int IN>
+static hipError_t launch_topk_in(const TopkParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.sq), block(kTopkThreads);
+  if (p.skv <= 8 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_reg_kernel<IN, 8>), grid, block, 0, s, p);
+  } else if (p.skv <= 16 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_reg_kernel<IN, 16>), grid, block, 0, s, p);
+  } else if (p.skv <= 32 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_reg_kernel<IN, 32>), grid, block, 0, s, p);
+  } else if (p.skv <= 64 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_reg_kernel<IN, 64>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL(topk_kernel<kF32>, dim3((unsigned)p.sq), dim3(kTopkThreads), 0, s, p);
+    hipLaunchKernelGGL((topk_stream_kernel<IN>), grid, block, 0, s, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_topk(int in_type, const TopkParams& p, hipStream_t s) {
+  if (p.sq == 0) return hipSuccess;
+  return in_type == kBF16 ? launch_topk_in<kBF16>(p, s) : launch_topk_in<kF32>(p, s);
 }
 
 }  // namespace mqa

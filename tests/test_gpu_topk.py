@@ -31,6 +31,10 @@ def _device():
     (33, 3000, 4096, False, 4),             # more than most rows hold
     (8, 65536, 2048, False, 5),
     (3, 1, 7, True, 6),
+    (20, 10000, 700, True, 7),              # the register kernel at each row capacity
+    (20, 20000, 2048, True, 8),
+    (6, 70001, 2048, True, 9),              # longer rows: the streaming kernel
+    (10, 20000, 5000, True, 10),            # topk past the LDS stage: the streaming kernel
 ])
 def test_topk_matches_oracle(sq, skv, topk, ranges, seed):
     import mqa_logits_amd as mq
@@ -67,6 +71,21 @@ def test_topk_all_equal_and_all_neg_inf_rows():
     got = mq.mqa_logits_topk(dev(x), 2048).cpu().numpy()
     assert np.array_equal(got, oracle.topk_indices(x, 2048))
     assert got[0].tolist() == list(range(2048)) and np.all(got[2] == -1)
+
+
+def test_topk_streaming_kernel_edge_rows():
+    # rows longer than the register kernel holds: an all-equal row (its top bin
+    # is too large for the LDS lists, so every level is a pass over the row),
+    # a row with fewer candidates than topk, and a random row
+    import mqa_logits_amd as mq
+    skv = 70000
+    x = np.full((3, skv), -np.inf, np.float32)
+    x[0] = 0.75
+    x[1, ::50] = np.arange(skv // 50, dtype=np.float32)
+    x[2] = np.random.default_rng(5).standard_normal(skv).astype(np.float32)
+    log("[topk] streaming kernel edge rows")
+    got = mq.mqa_logits_topk(dev(x), 3000).cpu().numpy()
+    assert np.array_equal(got, oracle.topk_indices(x, 3000))
 
 
 def test_topk_after_dense_logits_is_a_valid_selection():
