@@ -73,6 +73,22 @@ def test_topk_all_equal_and_all_neg_inf_rows():
     assert got[0].tolist() == list(range(2048)) and np.all(got[2] == -1)
 
 
+@pytest.mark.parametrize("skv", [1000, 10000, 30000, 60000, 70000])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_topk_many_keys_equal_to_the_cut(skv, bf16):
+    # values on a coarse grid: many keys equal the k-th largest, and equal keys
+    # keep appearing in columns after the ones taken (every kernel size)
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(skv + bf16)
+    x = (np.round(rng.standard_normal((4, skv)) * 2) / 2).astype(np.float32)
+    t = dev(x)
+    if bf16:
+        t = dev(synth.encode_bf16(x).view(np.int16)).view(torch.bfloat16)   # exact: few bits
+    log(f"[topk] ties at the cut skv={skv} bf16={bf16}")
+    got = mq.mqa_logits_topk(t, 1500).cpu().numpy()
+    assert np.array_equal(got, oracle.topk_indices(x, 1500))
+
+
 def test_topk_streaming_kernel_edge_rows():
     # rows longer than the register kernel holds: an all-equal row (its top bin
     # is too large for the LDS lists, so every level is a pass over the row),
