@@ -107,6 +107,16 @@ __device__ __forceinline__ v8i negate_fp8(const v8i& b, int mask) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
+// A wave-uniform 64-bit value loaded through the vector path (memory the
+// kernel also writes cannot be read on the scalar unit), moved to SGPRs so
+// that buffer resources built from it stay scalar: a resource in VGPRs makes
+// every access through it a loop over its distinct values.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float neg_inf() { return __uint_as_float(kNegInfBits); }
 
 __device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }

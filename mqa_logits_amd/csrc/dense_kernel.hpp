@@ -116,8 +116,8 @@ __device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int 
   int lane_off;                                // byte offset of (row g, column n), column 0
   char* const out_base = static_cast<char*>(p.out);
   if constexpr (STORE == kCompressed) {
-    const int64_t first = p.row_off[row0];
-    const int64_t last = p.row_off[min(row0 + kRowsPerWave, p.sq)];
+    const int64_t first = uniform64(p.row_off[row0]);
+    const int64_t last = uniform64(p.row_off[min(row0 + kRowsPerWave, p.sq)]);
     out_r = make_rsrc(out_base + first * kOB, (uint32_t)((last - first) * kOB));
     lane_off = (int)(row_ok ? (p.row_off[e_row_c] - first - s_row) * kOB : 0) + kOB * n;
   } else {
