@@ -216,17 +216,18 @@ struct RowGroup {
 
   // a_row(r) = the query row that A row r (0..3 -> lanes' (l>>2)&3) reads;
   // e_row = the query row whose outputs this lane accumulates (lane >> 4).
+  // The H heads held here are heads [h0, h0 + H) of rows of h_stride heads.
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
                                        const uint8_t* __restrict__ q_sf,
                                        const void* __restrict__ wts, bool w_bf16, int64_t a_row,
-                                       int64_t e_row, int lane) {
+                                       int64_t e_row, int lane, int h_stride = H, int h0 = 0) {
     using L = OperandLayout<FMT, D>;
     const int g = lane >> 4;
     const int lo = L::lo(g), hi = L::hi(g);
     const int head_lo = lane & 3;
 #pragma unroll
     for (int m = 0; m < kMT; ++m) {
-      const int64_t hr = a_row * H + 4 * m + head_lo;
+      const int64_t hr = a_row * h_stride + h0 + 4 * m + head_lo;
       const uint8_t* row = q + hr * L::kRowBytes;
       const uint4 a = lo >= 0 ? *reinterpret_cast<const uint4*>(row + lo) : zero4();
       const uint4 b = hi >= 0 ? *reinterpret_cast<const uint4*>(row + hi) : zero4();
@@ -246,7 +247,8 @@ struct RowGroup {
     for (int m = 0; m < kMT * kWays; ++m) asm volatile("" : "+a"(qa[m]));
     constexpr float kW = LIN ? 0.5f : 1.f;
     if (w_bf16) {
-      const uint2* wp = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(wts) + e_row * H);
+      const uint2* wp =
+          reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(wts) + e_row * h_stride + h0);
 #pragma unroll
       for (int i = 0; i < H / 4; ++i) {
         const uint2 v = wp[i];
@@ -256,7 +258,8 @@ struct RowGroup {
         w[4 * i + 3] = kW * bf16_value(v.y >> 16);
       }
     } else {
-      const float4* wp = reinterpret_cast<const float4*>(static_cast<const float*>(wts) + e_row * H);
+      const float4* wp =
+          reinterpret_cast<const float4*>(static_cast<const float*>(wts) + e_row * h_stride + h0);
 #pragma unroll
       for (int i = 0; i < H / 4; ++i) {
         const float4 v = wp[i];
@@ -385,10 +388,17 @@ struct KvOp {
 // Returns the first column not walked.
 // The ring's first kKvStages - 1 steps of a walk from cl (issued early, so
 // their latency overlaps whatever the caller still has to settle).
+// Issued in step order: the walk's loop waits for a step's operands by
+// counting the loads issued after them, and that count is fixed once for the
+// loop's first and later trips alike, so a first step issued last would make
+// every trip wait for all loads in flight.
 template <class Load>
 __device__ __forceinline__ void prefetch_span(int cl, KvOp (&o)[kKvStages], Load&& load) {
 #pragma unroll
-  for (int u = 0; u < kKvStages - 1; ++u) load(cl + u * kTileN, o[u]);
+  for (int u = 0; u < kKvStages - 1; ++u) {
+    load(cl + u * kTileN, o[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <bool FLIP, class RG, class Load, class Sink>

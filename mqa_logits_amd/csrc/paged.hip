@@ -20,11 +20,62 @@
 
 namespace mqa {
 
-template <int FMT, int H, int D, bool CLEAN, int OUT>
-__global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
+// Clean output of a head-split worker (HS = 2 below).  Each wave stages its
+// partial head sums of a trip (4 rows x kTripCols columns, -inf outside the
+// rows' ranges) in its own LDS buffers; after a barrier that both waves reach
+// once they have written the trip, a lane adds the two partials of one
+// 4-column group and stores it: wave w stores rows 2w and 2w + 1 from lanes
+// 0..31 (256-byte runs per row), lanes 32..63 store nothing.  Trips alternate
+// between two buffers, so a buffer is rewritten only after the next trip's
+// barrier, when both waves have read it.
+template <int OUT>
+struct PairSink {
+  float* mine;               // this wave's 2 x [4][kTripCols] floats
+  const float* other;        // the partner wave's
+  Rsrc r;
+  int base;                  // first column of the walk (trip-aligned)
+  int put_idx;               // this lane's slot: row g, column n of a trip's first step
+  int rd_idx;                // this lane's store group in a buffer
+  int row_off;               // byte offset of that group in the output at column 0
+  int last_j0;               // the group of trip j0 is stored iff base <= j0 <= last_j0
+  int rel_n, len;            // column j0 + n is in range iff j0 + rel_n in [0, len)
+  float4 pend;               // the last trip's sums, and their store offset
+  int pend_off;
+
+  __device__ __forceinline__ int half(int j0) const {
+    return (((j0 - base) >> 6) & 1) * (kRowsPerWave * kTripCols);
+  }
+  __device__ __forceinline__ void put(int u, int j0, float v) {
+    const bool in_range = (uint32_t)(j0 + rel_n) < (uint32_t)len;
+    mine[half(j0) + put_idx + u * kTileN] = in_range ? v : neg_inf();
+    if (u == 0) OutElem<OUT>::store4(r, pend_off, pend);
+  }
+  __device__ __forceinline__ void trip(int jt) {
+    // both waves' writes of trip jt are done (LDS only: the KV loads in
+    // flight are not waited for)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const float4 a = *reinterpret_cast<const float4*>(mine + half(jt) + rd_idx);
+    const float4 b = *reinterpret_cast<const float4*>(other + half(jt) + rd_idx);
+    pend = float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+    pend_off = (jt >= base && jt <= last_j0) ? row_off + OutElem<OUT>::kBytes * jt : kOOB;
+    asm volatile("" ::: "memory");
+  }
+  __device__ __forceinline__ void finish() { OutElem<OUT>::store4(r, pend_off, pend); }
+};
+
+// HS = 1: one wave per worker holds all H heads.  HS = 2 (clean output,
+// H = 64): the two waves of a block split the heads of one worker -- each
+// holds H / 2 heads' Q operands and weights, about half the registers, so two
+// workers share a SIMD and one's gather latency hides behind the other's
+// math -- walk the same blocks (the second read of a KV step comes from the
+// cache) and add their partial sums in PairSink.  Both waves take identical,
+// wave-uniform control flow, so they meet every barrier.
+template <int FMT, int H, int D, bool CLEAN, int OUT, int HS>
+__global__ __launch_bounds__(kWaveLanes * HS, HS) void paged_kernel(PagedParams p) {
+  static_assert(HS == 1 || (HS == 2 && CLEAN), "the head split writes clean logits only");
   // Decode batches are small: the weighted-query-sum launch would cost more
   // than the halved epilogue saves, so the paged kernel keeps max + fma.
-  using RG = RowGroup<FMT, H, D>;
+  using RG = RowGroup<FMT, H / HS, D>;
   using L = OperandLayout<FMT, D>;
   using OE = OutElem<OUT>;
   constexpr int kOB = OE::kBytes;              // bytes per logits element
@@ -33,7 +84,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
   constexpr int kBtWindow = kWaveLanes;        // block-table entries held per lane
 
   const int lane = threadIdx.x & (kWaveLanes - 1);
-  const int worker = blockIdx.x;                // one wave per block
+  const int wave = HS == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x;                // HS waves per block
   if (worker >= p.num_splits) return;
 
   const int g = lane >> 4;                 // output row (query token) of this lane in its group
@@ -60,8 +112,50 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
   const int eb = p.sched[2 * worker + 2];
   const int eblk = p.sched[2 * worker + 3];
 
-  __shared__ __attribute__((aligned(16))) float stage[2 * kRowsPerWave * kTripCols];
+  __shared__ __attribute__((aligned(16))) float stage_all[HS][2 * kRowsPerWave * kTripCols];
+  float* const stage = stage_all[wave];
   const float4 ninf4 = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+  if constexpr (CLEAN) {
+    // -inf for the blocks past each sequence's last one, round-robin over
+    // the waves of the launch: this wave owns units me, me + P, ...  Lane l
+    // looks up unit me + (64 k + l) P, so one load serves 64 units and no
+    // store waits on a load issued after it.  The fill goes first: at the
+    // wave's end it would add a store round trip to the launch's tail; here
+    // its stores drain while the first operands of the walk are loading.
+    const int64_t total = (int64_t)p.batch * p.nb_max;
+    const int64_t P = (int64_t)p.num_splits * HS;
+    for (int64_t f0 = worker + (int64_t)wave * p.num_splits; f0 < total; f0 += P * kWaveLanes) {
+      const int64_t f = f0 + (int64_t)lane * P;
+      int fb = 0, c = 0;
+      bool need = false;
+      if (f < total) {
+        fb = (int)(f / p.nb_max);
+        c = (int)(f - (int64_t)fb * p.nb_max);
+        const int len = clampi(p.ctx[fb], 0, p.max_ctx);
+        need = c >= ((len + bs - 1) >> bs_shift);
+      }
+      for (uint64_t m = __ballot(need); m != 0; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int ub = __builtin_amdgcn_readlane(fb, k);
+        const int uc = __builtin_amdgcn_readlane(c, k);
+        const Rsrc out_r = make_rsrc(static_cast<char*>(p.out) + (int64_t)ub * p.next_n * p.stride * kOB,
+                                     (uint32_t)(p.next_n * p.stride * kOB));
+        // 16-byte groups (lane l: row l / 16 of a 4-row group, columns
+        // 4 (l % 16) .. +3), then the 1..3 columns of a last group cut by max_ctx
+        const int c0 = uc << bs_shift;
+        const int c1 = min((uc + 1) << bs_shift, p.max_ctx);
+        for (int t0 = 0; t0 < p.next_n; t0 += kRowsPerWave) {
+          const bool row_ok = t0 + g < p.next_n;
+          const int t_e = min(t0 + g, p.next_n - 1);
+          const int grp_off = (t_e * (int)p.stride + 4 * n) * kOB;
+          for (int j0 = c0; j0 < c1; j0 += kTripCols)
+            OE::store4(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + kOB * j0 : kOOB, ninf4);
+          if ((c1 & 3) != 0 && row_ok && (c1 & ~3) + n < c1 && (c1 & ~3) >= c0)
+            OE::store1(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * kOB, neg_inf());
+        }
+      }
+    }
+  }
   RG rg;
   while (b < p.batch && (b < eb || (b == eb && blk < eblk))) {
     const int ctx = p.ctx[b];
@@ -80,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
       const bool row_ok = t0 + g < p.next_n;
       const int t_e = min(t0 + g, p.next_n - 1);
       const int t_a = min(t0 + ((lane >> 2) & 3), p.next_n - 1);
-      rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, r0 + t_a, r0 + t_e, lane);
+      rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, r0 + t_a, r0 + t_e, lane, H, wave * (H / HS));
       const int e_tok = clampi(ctx - p.next_n + t_e + 1, 0, len);   // this lane's row end
       const Rsrc out_r = make_rsrc(static_cast<char*>(p.out) + r0 * p.stride * kOB,
                                    (uint32_t)(p.next_n * p.stride * kOB));
@@ -116,7 +210,30 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
         constexpr bool kFlip = !FmtInfo<FMT>::kMX;
         KvOp o[kKvStages];
         prefetch_span(col0, o, load);
-        if constexpr (CLEAN) {
+        if constexpr (CLEAN && HS == 2) {
+          const int rs = 2 * wave + ((lane >> 4) & 1);   // the row this lane stores
+          const bool st_ok = lane < 32 && t0 + rs < p.next_n;
+          const int t_s = min(t0 + rs, p.next_n - 1);
+          const int last_j0 = st_ok ? (col1 & ~3) - 4 * n - 4 : -0x40000000;
+          PairSink<OUT> sink{stage,     stage_all[wave ^ 1], out_r,  col0,
+                             g * kTripCols + n, rs * kTripCols + 4 * n,
+                             (t_s * (int)p.stride + 4 * n) * kOB, last_j0, n, e_tok, ninf4, kOOB};
+          const int walked = compute_span<kFlip>(rg, col0, col1, o, load, sink);
+          if ((col1 & 3) != 0) {             // max_ctx not a multiple of 4: 1..3 columns
+            const int gs = col1 & ~3, jt = walked - kTripCols;
+            if (wave == 0 && row_ok && gs + n < col1) {
+              float v = neg_inf();
+              if (gs >= jt && gs < walked) {
+                const int i = sink.half(jt) + g * kTripCols + (gs - jt) + n;
+                v = stage_all[0][i] + stage_all[1][i];
+              }
+              OE::store1(out_r, (t_e * (int)p.stride + gs + n) * kOB, v);
+            }
+          }
+          // the partner's next walk rewrites its buffers only after this
+          // wave's last reads of them
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else if constexpr (CLEAN) {
           // Whole 16-byte groups of the window through LDS (lane l: row l / 16,
           // columns 4 (l % 16) .. +3 of a trip); in range iff column < e_tok.
           const int lim = col1 & ~3;
@@ -144,40 +261,20 @@ __global__ __launch_bounds__(kThreads, 1) void paged_kernel(PagedParams p) {
     }
     blk = seg_end;
   }
-
-  if constexpr (CLEAN) {
-    // -inf for the blocks past each sequence's last one, round-robin.
-    const int64_t total = (int64_t)p.batch * p.nb_max;
-    for (int64_t f = worker; f < total; f += p.num_splits) {
-      const int fb = (int)(f / p.nb_max);
-      const int c = (int)(f - (int64_t)fb * p.nb_max);
-      const int len = clampi(p.ctx[fb], 0, p.max_ctx);
-      if (c < ((len + bs - 1) >> bs_shift)) continue;
-      const Rsrc out_r = make_rsrc(static_cast<char*>(p.out) + (int64_t)fb * p.next_n * p.stride * kOB,
-                                   (uint32_t)(p.next_n * p.stride * kOB));
-      // 16-byte groups (lane l: row l / 16 of a 4-row group, columns
-      // 4 (l % 16) .. +3), then the 1..3 columns of a last group cut by max_ctx
-      const int c1 = min((c + 1) << bs_shift, p.max_ctx);
-      for (int t0 = 0; t0 < p.next_n; t0 += kRowsPerWave) {
-        const bool row_ok = t0 + g < p.next_n;
-        const int t_e = min(t0 + g, p.next_n - 1);
-        const int grp_off = (t_e * (int)p.stride + 4 * n) * kOB;
-        for (int j0 = c << bs_shift; j0 < c1; j0 += kTripCols)
-          OE::store4(out_r, (row_ok && j0 + 4 * n + 4 <= c1) ? grp_off + kOB * j0 : kOOB, ninf4);
-        if ((c1 & 3) != 0 && row_ok && (c1 & ~3) + n < c1 && (c1 & ~3) >= (c << bs_shift))
-          OE::store1(out_r, (t_e * (int)p.stride + (c1 & ~3) + n) * kOB, neg_inf());
-      }
-    }
-  }
 }
 
+// One block per worker: clean logits with 64 heads split the heads over two
+// waves, everything else runs one wave per worker.
 template <int FMT, int H, int D, int OUT>
 static hipError_t launch_paged_inst(int clean, const PagedParams& p, hipStream_t s) {
-  const int grid = (p.num_splits + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int grid = p.num_splits;
   if (clean) {
-    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
+    constexpr int kHS = H == 64 ? 2 : 1;
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true, OUT, kHS>), dim3(grid),
+                       dim3(kWaveLanes * kHS), 0, s, p);
   } else {
-    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false, OUT, 1>), dim3(grid), dim3(kWaveLanes), 0,
+                       s, p);
   }
   return hipGetLastError();
 }
