@@ -54,34 +54,55 @@ __global__ __launch_bounds__(1024) void compressed_offsets_kernel(const int32_t*
                                                                   const int32_t* __restrict__ ke,
                                                                   int32_t sq, int32_t skv,
                                                                   int64_t* __restrict__ off) {
-  __shared__ int64_t part[1024];
-  __shared__ int64_t carry_s;
-  const int t = threadIdx.x;
-  if (t == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < sq; base += 1024) {
-    const int i = base + t;
-    int64_t len = 0;
-    if (i < sq) {
-      const int s = clampi(ks[i], 0, skv);
-      const int e = clampi(ke[i], s, skv);
-      len = e - s;
+  // Thread t takes rows 4t .. 4t+3 of each round of 4096; a round is a scan
+  // of the threads' sums inside each wave (shuffles), then of the 16 wave
+  // totals, so it costs three barriers.
+  constexpr int kPer = 4;
+  constexpr int kWaves = 1024 / kWaveLanes;
+  __shared__ int64_t wsum[kWaves];
+  const int t = threadIdx.x, lane = t & (kWaveLanes - 1), wave = t / kWaveLanes;
+  int64_t carry = 0;
+  for (int base = 0; base < sq; base += 1024 * kPer) {
+    int64_t len[kPer], tsum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = base + kPer * t + k;
+      len[k] = 0;
+      if (i < sq) {
+        const int s = clampi(ks[i], 0, skv);
+        len[k] = clampi(ke[i], s, skv) - s;
+      }
+      tsum += len[k];
     }
-    part[t] = len;
-    __syncthreads();
-    for (int step = 1; step < 1024; step <<= 1) {     // inclusive scan
-      const int64_t v = t >= step ? part[t - step] : 0;
-      __syncthreads();
-      part[t] += v;
-      __syncthreads();
+    int64_t x = tsum;                          // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < kWaveLanes; d <<= 1) {
+      const int64_t y = __shfl_up(x, d);
+      if (lane >= d) x += y;
     }
-    const int64_t carry = carry_s;
-    if (i < sq) off[i] = carry + part[t] - len;
+    if (lane == kWaveLanes - 1) wsum[wave] = x;
     __syncthreads();
-    if (t == 1023) carry_s = carry + part[1023];
+    if (wave == 0) {                           // inclusive scan of the wave totals
+      int64_t v = lane < kWaves ? wsum[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kWaves; d <<= 1) {
+        const int64_t y = __shfl_up(v, d);
+        if (lane >= d) v += y;
+      }
+      if (lane < kWaves) wsum[lane] = v;
+    }
     __syncthreads();
+    int64_t excl = carry + (wave > 0 ? wsum[wave - 1] : 0) + x - tsum;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = base + kPer * t + k;
+      if (i < sq) off[i] = excl;
+      excl += len[k];
+    }
+    carry += wsum[kWaves - 1];
+    __syncthreads();                           // wsum is rewritten by the next round
   }
-  if (t == 0) off[sq] = carry_s;
+  if (t == 0) off[sq] = carry;
 }
 
 hipError_t launch_compressed_offsets(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,

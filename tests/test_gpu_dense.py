@@ -198,3 +198,19 @@ def test_compressed_guard_band():
     assert np.all(b[total:] == -3.0)
     ref, bound, _ = oracle.compressed_logits(*case.args())
     assert_close(b[:total], ref, bound, "compressed_guard")
+
+
+@pytest.mark.parametrize("sq", [1, 4095, 4096, 4097, 10000])
+def test_compressed_offsets_many_rounds(sq):
+    """Row offsets over several 4096-row scan rounds, with ragged, empty,
+    reversed and out-of-range ranges: bit-exact against the oracle."""
+    import mqa_logits_amd as mq
+    skv = 3000
+    rng = np.random.default_rng([77, sq])
+    ks = rng.integers(-100, skv + 100, size=sq).astype(np.int32)
+    ke = (ks + rng.integers(-50, 2000, size=sq)).astype(np.int32)
+    log(f"[compressed] offsets Sq={sq} Skv={skv}")
+    off = mq.mqa_logits_compressed_offsets(dev(ks), dev(ke), skv)
+    torch.cuda.synchronize()
+    ref = oracle.compressed_row_offsets(ks, ke, skv)
+    assert np.array_equal(off.cpu().numpy(), ref)
