@@ -8,12 +8,13 @@
 // made once per decoding step splits the (sequence, KV block) work list over
 // the workers (same PR, a97b74d Root cause / Fix).
 //
-// A worker is one wave.  One unit = one KV block for all next_n query rows of
-// a sequence (a single query atom: producer and consumer of the schedule
-// cannot disagree on atoms).  The wave holds 4 query rows at a time, so for
-// next_n > 4 it walks its run of blocks once per group of 4 rows; the re-read
-// blocks come from L2.  Columns past a sequence's last block are -inf fill
-// units spread round-robin over the workers in the same launch.
+// A worker is one block: one wave, or for clean logits with 64 heads two
+// waves that split the heads (paged_kernel below).  One unit = one KV block
+// for all next_n query rows of a sequence (a single query atom: producer and
+// consumer of the schedule cannot disagree on atoms).  A worker holds 4 query
+// rows at a time, so for next_n > 4 it walks its run of blocks once per group
+// of 4 rows; the re-read blocks come from L2.  Columns past a sequence's last
+// block are -inf fill units spread round-robin over the waves of the launch.
 #include "common.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
