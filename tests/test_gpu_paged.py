@@ -101,6 +101,17 @@ def test_paged_head_dim(h, d):
     _check(case, 16, f"paged_h{h}_d{d}")
 
 
+@pytest.mark.parametrize("splits", [1, 3000])
+def test_paged_edge_lengths_and_idle_workers(splits):
+    # empty, shorter-than-next_n and longer-than-max_context_len sequences, a
+    # width that is not a multiple of 4; one worker for everything, or far
+    # more workers than blocks (most walk nothing and only write -inf)
+    case = synth.paged_case(batch=6, next_n=4, h=64, d=128, block_size=64, num_blocks=200,
+                            ctx_lo=1, ctx_hi=10, max_context_len=1030, seed=61,
+                            context_lens=[0, 2, 1030, 5000, 64, 65])
+    _check(case, splits, f"paged_edges_s{splits}")
+
+
 def test_paged_negative_scales_and_keep_mode():
     case = synth.paged_case(batch=3, next_n=4, h=64, d=128, block_size=64, num_blocks=100,
                             ctx_lo=100, ctx_hi=1000, max_context_len=1024, seed=5,
