@@ -240,8 +240,9 @@ mqa_status paged_mqa_logits(mqa_dtype dt,
  * article's paged example); negative on error. */
 int32_t mqa_num_cus(int32_t device);
 
-/* A good num_splits for paged_mqa_logits on a device: one per wave slot the
- * paged kernel keeps resident (4 per compute unit); negative on error. */
+/* A good num_splits for paged_mqa_logits on a device: 4 workers per compute
+ * unit, all resident at once (a worker is one wave, or two waves that split
+ * 64 heads, whose registers allow two workers per SIMD); negative on error. */
 int32_t paged_mqa_logits_default_splits(int32_t device);
 
 /* Thread-local description of the last non-OK status ("" if none). */
