@@ -85,12 +85,12 @@ mqa_status check_common(mqa_dtype dt, const void* q, const uint8_t* q_sf, const 
 
 // Chunks per row group: about one wave per SIMD (a single dispatch round, one
 // prologue per SIMD; the chunks of a row group carry equal work), with runs
-// of at least 256 tokens.
+// of at least one 64-token trip (few rows: more, shorter chunks).
 int32_t pick_chunks(int32_t sq, int32_t skv) {
   constexpr int64_t kTargetBlocks = 1024 / mqa::kDenseWaves;
   const int64_t qblocks = (sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves);
   int64_t n_chunks = (kTargetBlocks + qblocks - 1) / qblocks;
-  const int64_t max_chunks = (skv + 255) / 256;
+  const int64_t max_chunks = (skv + 63) / 64;
   if (n_chunks > max_chunks) n_chunks = max_chunks;
   if (n_chunks < 1) n_chunks = 1;
   return (int32_t)n_chunks;
