@@ -32,7 +32,8 @@ METRIC = "MQA-logits effective TFLOP/s + % fp8 MFMA peak (H64 D128, 2K×32K)"
 PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 PEAK_HBM_GBS = 8000.0
 
-WORKLOADS = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4-mxfp8": 4, "c4-mxfp4": 4}
+WORKLOADS = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4-mxfp8": 4, "c4-mxfp4": 4,
+             "c1-mxfp8": 1, "c1-mxfp4": 1}
 
 
 def log(*a):
@@ -168,7 +169,7 @@ def check_mask(out, case, rows_per_chunk=128):
             raise SystemExit(f"mask check failed in rows [{r0}, {r1})")
 
 
-def build_step(name, schedule=False, logits_dtype="fp32"):
+def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
     """Returns (step_fn, info dict) with inputs resident on cuda:0.
 
     schedule: dense / compressed calls follow a work schedule made by
@@ -182,10 +183,10 @@ def build_step(name, schedule=False, logits_dtype="fp32"):
     out_size = 4 if logits_dtype == "fp32" else 2
 
     idx = WORKLOADS[name]
-    fmt = name.split("-")[1] if name.startswith("c4") else None
-    case = synth.config_case(idx, fmt)
+    fmt = name.split("-")[1] if "-" in name else None
+    case = synth.config_case(idx, fmt, zero=zero)
     dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    info = dict(workload=synth.CONFIG_NAMES[idx] + (f"_{fmt}" if fmt else ""), case=case)
+    info = dict(workload=case.name + ("_zero" if zero else ""), case=case)
 
     def dense_schedule(ks, ke):
         if not schedule:
@@ -358,6 +359,9 @@ def main():
     ap.add_argument("--schedule", action="store_true",
                     help="dense/compressed calls follow an mqa_logits_metadata work schedule")
     ap.add_argument("--logits-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--zero", action="store_true",
+                    help="all-zero Q, KV and weights with unit scales (the pages' timing "
+                         "workload; dense workloads only)")
     ap.add_argument("--topk", type=int, default=0, metavar="K",
                     help="also time mqa_logits_topk(K) over a step's logits (reported apart)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -380,7 +384,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n,
                           "launches": (args.warmup or 0) + args.steps}), flush=True)
         return
-    step, info = build_step(args.workload, args.schedule, args.logits_dtype)
+    step, info = build_step(args.workload, args.schedule, args.logits_dtype, args.zero)
+    if args.zero:
+        info["cfg"]["inputs"] = "all_zero"
     if args.warmup is not None:
         for _ in range(args.warmup):
             step()

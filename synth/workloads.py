@@ -247,30 +247,37 @@ CONFIG_NAMES = {
 }
 
 
-def config_case(idx, fmt=None):
+def config_case(idx, fmt=None, zero=False):
     """The five workloads, seeded with 1000 + idx.  idx 4 takes fmt
-    'mxfp8' (default) or 'mxfp4'."""
+    'mxfp8' (default) or 'mxfp4'; idx 1 takes 'fp8' (default), 'mxfp8' or
+    'mxfp4' (the shape the pages time their MX kernels on).  zero: the dense
+    workloads with all-zero Q, KV and weights and unit MX scales (the pages'
+    timing workload)."""
     seed = 1000 + idx
+    if zero and idx == 3:
+        raise ValueError("the paged workload has no all-zero variant")
     if idx == 0:
         sq, skv = 256, 1024
-        return dense_case(sq, skv, 16, 64, "fp8", seed,
-                          k_end=skv - sq + np.arange(sq) + 1, name=CONFIG_NAMES[0])
+        return dense_case(sq, skv, 16, 64, "fp8", seed, k_end=skv - sq + np.arange(sq) + 1,
+                          zero=zero, name=CONFIG_NAMES[0])
     if idx == 1:
+        fmt = fmt or "fp8"
         sq, skv = 2048, 32768
-        return dense_case(sq, skv, 64, 128, "fp8", seed,
-                          k_end=skv - sq + np.arange(sq), name=CONFIG_NAMES[1])
+        name = CONFIG_NAMES[1] if fmt == "fp8" else CONFIG_NAMES[1].replace("_fp8", "_" + fmt)
+        return dense_case(sq, skv, 64, 128, fmt, seed, k_end=skv - sq + np.arange(sq),
+                          zero=zero, name=name)
     if idx == 2:
         sq, skv = 2048, 4096
-        return dense_case(sq, skv, 32, 64, "fp8", seed,
-                          k_start=np.arange(sq), k_end=np.full(sq, skv), name=CONFIG_NAMES[2])
+        return dense_case(sq, skv, 32, 64, "fp8", seed, k_start=np.arange(sq),
+                          k_end=np.full(sq, skv), zero=zero, name=CONFIG_NAMES[2])
     if idx == 3:
         return paged_case(64, 4, 64, 128, 64, 36000, 1024, 32768, 32768, "fp8", seed,
                           name=CONFIG_NAMES[3])
     if idx == 4:
         fmt = fmt or "mxfp8"
         sq, skv = 8192, 65536
-        return dense_case(sq, skv, 64, 128, fmt, seed,
-                          k_end=skv - sq + np.arange(sq), name=CONFIG_NAMES[4] + "_" + fmt)
+        return dense_case(sq, skv, 64, 128, fmt, seed, k_end=skv - sq + np.arange(sq),
+                          zero=zero, name=CONFIG_NAMES[4] + "_" + fmt)
     raise ValueError(idx)
 
 
