@@ -33,7 +33,7 @@ PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4-mxfp8": 4, "c4-mxfp4": 4,
-             "c1-mxfp8": 1, "c1-mxfp4": 1}
+             "c1-mxfp8": 1, "c1-mxfp4": 1, "c3-mxfp8": 3, "c3-mxfp4": 3}
 
 
 def log(*a):

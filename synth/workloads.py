@@ -249,8 +249,8 @@ CONFIG_NAMES = {
 
 def config_case(idx, fmt=None, zero=False):
     """The five workloads, seeded with 1000 + idx.  idx 4 takes fmt
-    'mxfp8' (default) or 'mxfp4'; idx 1 takes 'fp8' (default), 'mxfp8' or
-    'mxfp4' (the shape the pages time their MX kernels on).  zero: the dense
+    'mxfp8' (default) or 'mxfp4'; idx 1 and 3 take 'fp8' (default), 'mxfp8'
+    or 'mxfp4' (idx 1: the shape the pages time their MX kernels on).  zero: the dense
     workloads with all-zero Q, KV and weights and unit MX scales (the pages'
     timing workload)."""
     seed = 1000 + idx
@@ -271,8 +271,9 @@ def config_case(idx, fmt=None, zero=False):
         return dense_case(sq, skv, 32, 64, "fp8", seed, k_start=np.arange(sq),
                           k_end=np.full(sq, skv), zero=zero, name=CONFIG_NAMES[2])
     if idx == 3:
-        return paged_case(64, 4, 64, 128, 64, 36000, 1024, 32768, 32768, "fp8", seed,
-                          name=CONFIG_NAMES[3])
+        fmt = fmt or "fp8"
+        name = CONFIG_NAMES[3] if fmt == "fp8" else CONFIG_NAMES[3].replace("_fp8", "_" + fmt)
+        return paged_case(64, 4, 64, 128, 64, 36000, 1024, 32768, 32768, fmt, seed, name=name)
     if idx == 4:
         fmt = fmt or "mxfp8"
         sq, skv = 8192, 65536

@@ -36,3 +36,14 @@ def test_all_zero_variant(idx, fmt):
 def test_paged_has_no_all_zero_variant():
     with pytest.raises(ValueError):
         synth.config_case(3, zero=True)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_config3_shape_in_mx_formats(fmt):
+    case = synth.config_case(3, fmt)
+    ref = synth.config_case(3)
+    assert case.fmt == fmt and case.name.endswith("_" + fmt)
+    assert case.kv_scale_pool is None and case.kv_sf_pool is not None
+    # the same sequences and block table as config 3
+    assert np.array_equal(case.context_lens, ref.context_lens)
+    assert np.array_equal(case.block_table, ref.block_table)
