@@ -139,3 +139,12 @@ def test_config3_paged_decode_full_parity_and_split_independence():
     for other in (97, 2 * splits):
         out2, _ = _run(case, other)
         assert torch.equal(out.view(torch.int32), out2.view(torch.int32)), f"splits={other}"
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_config3_shape_in_mx_formats_full_parity(fmt):
+    # the paged decode workload at full size in the MX formats (the two-wave
+    # head split with e8m0 block scales), every row against the oracle
+    case = synth.config_case(3, fmt)
+    import mqa_logits_amd as mq
+    _check(case, mq.paged_mqa_logits_default_splits(0), f"config3_{fmt}")
