@@ -132,15 +132,18 @@ def test_bitwise_determinism_20_repeats():
             assert torch.equal(out.view(torch.int32), first.view(torch.int32))
 
 
-def test_config1_prefill_sampled_rows_and_full_mask():
-    case = synth.config_case(1)
-    log("[dense] config 1 full size")
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
+def test_config1_prefill_sampled_rows_and_full_mask(fmt):
+    # fp8 is config 1; the MX formats run its shape (two column chunks per
+    # row group, where config 4 takes one)
+    case = synth.config_case(1, fmt)
+    log(f"[dense] config 1 full size, {fmt}")
     out = run_dense(case)
     torch.cuda.synchronize()
     assert_mask_on_device(out, case.k_start, case.k_end, case.skv)
     rows = synth.sampled_rows(case.seed, case.sq, 24)
     ref, bound = oracle.dense_logits(*case.args(), rows=rows)
-    assert_close(out[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, bound, "config1_rows")
+    assert_close(out[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, bound, f"config1_rows_{fmt}")
     # 4096 sampled rows, a few sampled columns each (always one near the end)
     srows = synth.sampled_rows(case.seed, case.sq, 4096)
     rng = np.random.default_rng(case.seed)
@@ -149,7 +152,7 @@ def test_config1_prefill_sampled_rows_and_full_mask():
     c[::4] = np.maximum(0, case.k_end[srows] - 1)
     v, b = oracle.dense_entries(*case.args(), r, c)
     got = out[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()].cpu().numpy()
-    assert_close(got, v, b, "config1_entries")
+    assert_close(got, v, b, f"config1_entries_{fmt}")
 
 
 # ---------------------------------------------------------------------------
