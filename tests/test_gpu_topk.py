@@ -35,6 +35,9 @@ def _device():
     (20, 20000, 2048, True, 8),
     (6, 70001, 2048, True, 9),              # longer rows: the streaming kernel
     (10, 20000, 5000, True, 10),            # topk past the LDS stage: the streaming kernel
+    (520, 20000, 2048, True, 12),           # more rows than two per compute unit
+    (5, 40000, 1001, True, 13),             # an odd topk
+    (7, 24577, 4096, True, 14),             # a large topk over long rows
 ])
 def test_topk_matches_oracle(sq, skv, topk, ranges, seed):
     import mqa_logits_amd as mq
