@@ -26,6 +26,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmqa_logits.so")
 
 FORMATS = {"fp8": 0, "mxfp8": 1, "mxfp4": 2}
+# mqa_precision of the C ABI: the matrix core's grouped summation, or every
+# product exact (eight KV operand copies for fp8 elements)
+PRECISIONS = {"default": 0, "exact": 1}
 # mqa_float of the C ABI: element type of the weights and of the logits
 FLOAT_TYPES = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -47,15 +50,15 @@ def _load():
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sigs = {
         "mqa_logits": [I32, P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, I32, I32, I32,
-                       P, I32, P],
+                       P, I32, I32, P],
         "mqa_logits_metadata": [P, P, I32, I32, I32, P, P],
         "mqa_logits_topk": [P, I32, I64, P, P, I32, I32, I32, P, I64, P],
         "mqa_logits_compressed_offsets": [P, P, I32, I32, P, P],
         "mqa_logits_compressed": [I32, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
-                                  P, I32, P],
+                                  P, I32, I32, P],
         "paged_mqa_logits_metadata": [P, I32, I32, I32, I32, I32, P, P],
         "paged_mqa_logits": [I32, P, P, P, P, P, P, P, P, I64, P, P, I64,
-                             I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, P],
+                             I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, P],
     }
     for name, argtypes in sigs.items():
         fn = getattr(lib, name)
@@ -103,6 +106,12 @@ def _fmt(fmt):
     if fmt not in FORMATS:
         raise ValueError(f"format must be one of {sorted(FORMATS)}, got {fmt!r}")
     return FORMATS[fmt]
+
+
+def _precision(precision):
+    if precision not in PRECISIONS:
+        raise ValueError(f"precision must be one of {sorted(PRECISIONS)}, got {precision!r}")
+    return PRECISIONS[precision]
 
 
 def _head_dim(fmt, q):
@@ -155,10 +164,12 @@ def mqa_logits_metadata(k_start, k_end, skv, num_splits=None, out=None):
 
 
 def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
-               clean_logits=True, out=None, logits_dtype=torch.float32, schedule=None):
+               clean_logits=True, out=None, logits_dtype=torch.float32, schedule=None,
+               precision="default"):
     """Dense logits [Sq, Skv] of logits_dtype (out may be a wider-strided row
     view; its dtype then decides).  weights: float32 or bfloat16.  schedule:
-    None or mqa_logits_metadata's result for the same ranges."""
+    None or mqa_logits_metadata's result for the same ranges.  precision:
+    "default" or "exact" (mqa_precision)."""
     sq, h = weights.shape
     skv = kv.shape[0]
     if out is None:
@@ -170,7 +181,8 @@ def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
         _ptr(weights), _ptr(k_start), _ptr(k_end), ctypes.c_void_p(out.data_ptr()),
         out.stride(0) if sq > 0 else skv, sq, skv, h, _head_dim(fmt, q),
         1 if clean_logits else 0, _float_type(weights.dtype, "weights"),
-        _float_type(out.dtype, "logits"), *_schedule(schedule), _stream(q)))
+        _float_type(out.dtype, "logits"), *_schedule(schedule), _precision(precision),
+        _stream(q)))
     return out
 
 
@@ -202,7 +214,7 @@ def mqa_logits_compressed_offsets(k_start, k_end, skv, out=None):
 
 def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
                           row_offsets=None, out=None, logits_dtype=torch.float32,
-                          schedule=None):
+                          schedule=None, precision="default"):
     """Packed logits; returns (packed [total] of logits_dtype, row_offsets int64
     [Sq+1]).
 
@@ -217,7 +229,8 @@ def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv), _ptr(kv_sf), _ptr(kv_scale),
         _ptr(weights), _ptr(k_start), _ptr(k_end), _ptr(row_offsets), _ptr(out),
         sq, skv, h, _head_dim(fmt, q), _float_type(weights.dtype, "weights"),
-        _float_type(out.dtype, "logits"), *_schedule(schedule), _stream(q)))
+        _float_type(out.dtype, "logits"), *_schedule(schedule), _precision(precision),
+        _stream(q)))
     return out, row_offsets
 
 
@@ -236,7 +249,8 @@ def paged_mqa_logits_metadata(context_lens, next_n, block_size, max_context_len,
 
 def paged_mqa_logits(fmt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
                      context_lens, block_table, schedule, next_n, max_context_len,
-                     clean_logits=True, out=None, logits_dtype=torch.float32):
+                     clean_logits=True, out=None, logits_dtype=torch.float32,
+                     precision="default"):
     """Paged decode logits [batch * next_n, max_context_len] of logits_dtype."""
     batch = context_lens.shape[0]
     rows, h = weights.shape
@@ -252,5 +266,5 @@ def paged_mqa_logits(fmt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
         _ptr(schedule), ctypes.c_void_p(out.data_ptr()), out.stride(0), batch, next_n, h,
         _head_dim(fmt, q), block_size, num_blocks, max_context_len, num_splits,
         1 if clean_logits else 0, _float_type(weights.dtype, "weights"),
-        _float_type(out.dtype, "logits"), _stream(q)))
+        _float_type(out.dtype, "logits"), _precision(precision), _stream(q)))
     return out

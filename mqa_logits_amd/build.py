@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmqa_logits.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dense.hip", "dense_bf16.hip", "dense_sched.hip", "dense_sched_bf16.hip", "qsum.hip",
+SOURCES = ["dense.hip", "dense_bf16.hip", "dense_sched.hip", "dense_sched_bf16.hip",
            "topk.hip", "paged.hip", "api.cpp"]
 # measurement aid for bench.py, linked into a library of its own
 PROBE_SOURCES = ["peak.hip"]

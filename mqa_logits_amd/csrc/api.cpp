@@ -8,10 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
-#include <map>
-#include <mutex>
 #include <string>
-#include <utility>
 
 #include "launch.hpp"
 
@@ -96,56 +93,6 @@ int32_t pick_chunks(int32_t sq, int32_t skv) {
   return (int32_t)n_chunks;
 }
 
-// Workspace of the weighted query sum, one per (device, stream): work on a
-// stream runs in order, so consecutive calls on it can share one buffer, and
-// a steady sequence of calls allocates nothing.  It grows when a call needs
-// more (hipFree of the old one waits for the work using it) and lives until
-// the process ends.
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
-
-hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  auto& slot = g_ws[{dev, stream}];
-  if (slot.second < bytes) {
-    if (slot.first) {
-      e = hipFree(slot.first);
-      slot = {nullptr, 0};
-      if (e != hipSuccess) return e;
-    }
-    void* p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    slot = {p, bytes};
-  }
-  *out = slot.first;
-  return hipSuccess;
-}
-
-// H = 64: the kernels take the linear half of ReLU from the weighted query
-// sum's pieces (qsum.hip), written into the stream's workspace right before
-// the launch that reads them.
-template <class Launch>
-mqa_status with_qsum(mqa_dtype dt, const void* q, const uint8_t* q_sf, const void* weights,
-                     int32_t w_bf16, int32_t rows, int32_t d, const uint8_t** ql,
-                     const uint8_t** ql_sf, hipStream_t stream, const char* who,
-                     Launch&& launch) {
-  const size_t ql_bytes = (size_t)rows * 4 * d, sf_bytes = (size_t)rows * 4 * (d / 32);
-  void* ws = nullptr;
-  hipError_t e = workspace(stream, ql_bytes + sf_bytes + 16, &ws);
-  if (e != hipSuccess) return hip_status(e, who);
-  mqa::QsumParams qp{static_cast<const uint8_t*>(q), q_sf, weights, static_cast<uint8_t*>(ws),
-                     static_cast<uint8_t*>(ws) + ql_bytes, rows, w_bf16};
-  *ql = qp.ql;
-  *ql_sf = qp.ql_sf;
-  e = mqa::launch_qsum((int)dt, d, qp, stream);
-  if (e == hipSuccess) e = launch();
-  return hip_status(e, who);
-}
-
 // The dense work schedule (mqa_logits_metadata): 4-row groups, at most
 // kMaxSchedGroups of them (the metadata kernel's prefix lives in LDS), and a
 // unit total that fits int32.
@@ -168,8 +115,8 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
                      mqa_float weights_type, const int32_t* k_start, const int32_t* k_end,
                      const int64_t* row_off, void* out, mqa_float logits_type, int64_t stride,
                      int32_t sq, int32_t skv, int32_t h, int32_t d, int store,
-                     const int32_t* schedule, int32_t num_splits, hipStream_t stream,
-                     const char* who) {
+                     const int32_t* schedule, int32_t num_splits, int32_t exact,
+                     hipStream_t stream, const char* who) {
   if (schedule) {
     mqa_status st = check_dense_schedule(sq, skv, num_splits, who);
     if (st != MQA_OK) return st;
@@ -196,6 +143,7 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   p.w_bf16 = weights_type == MQA_BF16;
   p.sched = schedule;
   p.num_splits = schedule ? num_splits : 0;
+  p.exact = exact;
   const int out_type = logits_type == MQA_BF16 ? mqa::kBF16 : mqa::kF32;
   const int64_t grid =
       schedule ? ((int64_t)num_splits + mqa::kDenseWaves - 1) / mqa::kDenseWaves
@@ -203,13 +151,17 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   if (grid > 0x7fffffff) return fail(MQA_ERR_UNSUPPORTED, "%s: problem too large", who);
   if (debug_enabled())
     fprintf(stderr,
-            "[mqa_logits] %s dt=%d H=%d D=%d store=%d w=%d out=%d Sq=%d Skv=%d chunks=%d grid=%lld\n",
-            who, (int)dt, h, d, store, (int)weights_type, (int)logits_type, sq, skv, p.n_chunks,
-            (long long)grid);
-  if (h != mqa::kLinHeads)
-    return hip_status(mqa::launch_dense((int)dt, h, d, store, out_type, p, stream), who);
-  return with_qsum(dt, q, q_sf, weights, p.w_bf16, sq, d, &p.ql, &p.ql_sf, stream, who,
-                   [&] { return mqa::launch_dense((int)dt, h, d, store, out_type, p, stream); });
+            "[mqa_logits] %s dt=%d H=%d D=%d store=%d w=%d out=%d exact=%d Sq=%d Skv=%d chunks=%d "
+            "grid=%lld\n",
+            who, (int)dt, h, d, store, (int)weights_type, (int)logits_type, exact, sq, skv,
+            p.n_chunks, (long long)grid);
+  return hip_status(mqa::launch_dense((int)dt, h, d, store, out_type, p, stream), who);
+}
+
+mqa_status check_precision(mqa_precision precision, const char* who) {
+  if (precision != MQA_PRECISION_DEFAULT && precision != MQA_PRECISION_EXACT_PRODUCTS)
+    return fail(MQA_ERR_INVALID_ARG, "%s: unknown precision %d", who, (int)precision);
+  return MQA_OK;
 }
 
 }  // namespace
@@ -238,12 +190,15 @@ mqa_status mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const vo
                       const int32_t* k_start, const int32_t* k_end, void* logits,
                       int64_t logits_stride, int32_t sq, int32_t skv, int32_t h, int32_t d,
                       int32_t clean_logits, mqa_float weights_type, mqa_float logits_type,
-                      const int32_t* schedule, int32_t num_splits, hipStream_t stream) {
+                      const int32_t* schedule, int32_t num_splits, mqa_precision precision,
+                      hipStream_t stream) {
   const char* who = "mqa_logits";
   if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
   if (logits_stride < skv) return fail(MQA_ERR_INVALID_ARG, "%s: logits_stride < Skv", who);
+  mqa_status st = check_precision(precision, who);
+  if (st != MQA_OK) return st;
   if (sq == 0 || skv == 0) return ok();
-  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type,
+  st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type,
                                logits_type, h, d, who);
   if (st != MQA_OK) return st;
   if (!k_start || !k_end || !logits) return fail(MQA_ERR_INVALID_ARG, "%s: null ranges or logits", who);
@@ -256,7 +211,7 @@ mqa_status mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, const vo
   return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type, k_start, k_end,
                    nullptr, logits, logits_type, logits_stride, sq, skv, h, d,
                    clean_logits ? mqa::kDenseClean : mqa::kDenseKeep, schedule, num_splits,
-                   stream, who);
+                   precision == MQA_PRECISION_EXACT_PRODUCTS, stream, who);
 }
 
 mqa_status mqa_logits_compressed_offsets(const int32_t* k_start, const int32_t* k_end, int32_t sq,
@@ -276,11 +231,14 @@ mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_s
                                  const int64_t* row_offsets, void* logits_packed, int32_t sq,
                                  int32_t skv, int32_t h, int32_t d, mqa_float weights_type,
                                  mqa_float logits_type, const int32_t* schedule,
-                                 int32_t num_splits, hipStream_t stream) {
+                                 int32_t num_splits, mqa_precision precision,
+                                 hipStream_t stream) {
   const char* who = "mqa_logits_compressed";
   if (sq < 0 || skv < 0) return fail(MQA_ERR_INVALID_ARG, "%s: negative Sq or Skv", who);
+  mqa_status st = check_precision(precision, who);
+  if (st != MQA_OK) return st;
   if (sq == 0 || skv == 0) return ok();
-  mqa_status st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type,
+  st = check_common(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type,
                                logits_type, h, d, who);
   if (st != MQA_OK) return st;
   if (!k_start || !k_end || !row_offsets || !logits_packed)
@@ -290,7 +248,7 @@ mqa_status mqa_logits_compressed(mqa_dtype dt, const void* q, const uint8_t* q_s
     return fail(MQA_ERR_INVALID_ARG, "%s: misaligned pointer", who);
   return run_dense(dt, q, q_sf, kv, kv_sf, kv_scale, weights, weights_type, k_start, k_end,
                    row_offsets, logits_packed, logits_type, 0, sq, skv, h, d, mqa::kCompressed,
-                   schedule, num_splits, stream, who);
+                   schedule, num_splits, precision == MQA_PRECISION_EXACT_PRODUCTS, stream, who);
 }
 
 mqa_status mqa_logits_topk(const void* logits, mqa_float logits_type, int64_t logits_stride,
@@ -380,9 +338,11 @@ mqa_status paged_mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, co
                             int32_t batch, int32_t next_n, int32_t h, int32_t d,
                             int32_t block_size, int32_t num_blocks, int32_t max_context_len,
                             int32_t num_splits, int32_t clean_logits, mqa_float weights_type,
-                            mqa_float logits_type, hipStream_t stream) {
+                            mqa_float logits_type, mqa_precision precision, hipStream_t stream) {
   const char* who = "paged_mqa_logits";
   mqa_status st = check_paged_shape(batch, next_n, block_size, max_context_len, num_splits, who);
+  if (st != MQA_OK) return st;
+  st = check_precision(precision, who);
   if (st != MQA_OK) return st;
   st = check_common(dt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights, weights_type,
                     logits_type, h, d, who);
@@ -426,9 +386,10 @@ mqa_status paged_mqa_logits(mqa_dtype dt, const void* q, const uint8_t* q_sf, co
   p.num_splits = num_splits;
   p.nb_max = (int32_t)nb_max;
   p.w_bf16 = weights_type == MQA_BF16;
+  p.exact = precision == MQA_PRECISION_EXACT_PRODUCTS;
   if (debug_enabled())
-    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d batch=%d next_n=%d bs=%d splits=%d\n", who,
-            (int)dt, h, d, batch, next_n, block_size, num_splits);
+    fprintf(stderr, "[mqa_logits] %s dt=%d H=%d D=%d batch=%d next_n=%d bs=%d splits=%d exact=%d\n",
+            who, (int)dt, h, d, batch, next_n, block_size, num_splits, p.exact);
   const int out_type = logits_type == MQA_BF16 ? mqa::kBF16 : mqa::kF32;
   return hip_status(mqa::launch_paged((int)dt, h, d, clean_logits ? 1 : 0, out_type, p, stream),
                     who);

@@ -7,7 +7,7 @@
 namespace mqa {
 
 hipError_t launch_dense_f32(int fmt, int h, int d, int store, const DenseParams& p, hipStream_t s) {
-  return dispatch_fmt<kF32, false>(fmt, h, d, store, p, s);
+  return dispatch_fmt<kF32, false>(fmt, h, d, store, p.exact != 0, p, s);
 }
 
 hipError_t launch_dense(int fmt, int h, int d, int store, int out, const DenseParams& p,

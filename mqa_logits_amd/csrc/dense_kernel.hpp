@@ -47,11 +47,23 @@ __device__ __forceinline__ int group_trips(int lo, int hi) {
   return (hi - lo64 + kTripCols - 1) / kTripCols;
 }
 
+// Arithmetic of an instance: EXACT splits the KV operand so that every
+// product reaches the accumulator exactly (always for H <= 16, whose few
+// heads leave the tolerance too little room for the matrix core's grouped
+// summation; on request otherwise); LIN takes ReLU's linear half from the
+// weighted query sum (H = 64, not EXACT: the sum is rounded to e4m3 pieces).
+template <int H, bool EXACT>
+struct DenseMode {
+  static constexpr bool kExact = EXACT || H <= 16;
+  static constexpr bool kLin = H == kLinHeads && !kExact;
+};
+
 // One wave's piece of row group row0 / 4; seg(trips) -> GroupSeg picks it.
-template <int FMT, int H, int D, int STORE, int OUT, class SegFn>
+template <int FMT, int H, int D, int STORE, int OUT, bool EXACT, class SegFn>
 __device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int wave, int lane,
                                             SegFn&& seg) {
-  using RG = RowGroup<FMT, H, D, H == kLinHeads>;
+  using M = DenseMode<H, EXACT>;
+  using RG = RowGroup<FMT, H, D, M::kLin, M::kExact>;
   using L = OperandLayout<FMT, D>;
   using OE = OutElem<OUT>;
   constexpr int kNKB = RG::kNKB;
@@ -79,8 +91,12 @@ __device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int 
   __builtin_amdgcn_sched_barrier(0);
 
   RG rg;
-  rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, a_row_c, e_row_c, lane);
-  rg.load_lin(p.ql, p.ql_sf, a_row_c, lane);
+  char* lin_lds = nullptr;
+  if constexpr (M::kLin) {
+    __shared__ __attribute__((aligned(16))) char lin_all[kDenseWaves][LinLds<D>::kBytes];
+    lin_lds = lin_all[wave];
+  }
+  rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, a_row_c, e_row_c, lane, H, 0, lin_lds);
   __builtin_amdgcn_sched_barrier(0);
 
   // The ranges, their union, and this lane's row.
@@ -242,7 +258,7 @@ __device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int 
 // run) takes chunk b % n_chunks of 4 consecutive row groups, one per wave;
 // the union of a group's ranges splits into n_chunks runs of whole trips of
 // nearly equal length, so the chunks of a group do the same MFMA work.
-template <int FMT, int H, int D, int STORE, int OUT>
+template <int FMT, int H, int D, int STORE, int OUT, bool EXACT>
 __global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) {
   const int lane = threadIdx.x & (kWaveLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) 
   const int chunk = bid - rblock * p.n_chunks;
   const int row0 = (rblock * kDenseWaves + wave) * kRowsPerWave;
   if (row0 >= p.sq) return;
-  dense_group<FMT, H, D, STORE, OUT>(p, row0, wave, lane, [&](int trips) {
+  dense_group<FMT, H, D, STORE, OUT, EXACT>(p, row0, wave, lane, [&](int trips) {
     return GroupSeg{(int)((int64_t)chunk * trips / p.n_chunks),
                     (int)((int64_t)(chunk + 1) * trips / p.n_chunks), chunk == 0,
                     chunk == p.n_chunks - 1};
@@ -269,7 +285,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) 
 // -inf fill).  Its entries schedule[worker] = (g, t) and schedule[worker + 1]
 // bound the piece.  Entries are clamped, and every iteration moves to the next
 // group, so any schedule contents stay in bounds and the loop ends.
-template <int FMT, int H, int D, int STORE, int OUT>
+template <int FMT, int H, int D, int STORE, int OUT, bool EXACT>
 __global__ __launch_bounds__(kDenseThreads, 1) void dense_sched_kernel(DenseParams p) {
   const int lane = threadIdx.x & (kWaveLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_sched_kernel(DensePara
   const int et = max(p.sched[2 * worker + 3], 0);
   for (; grp < n_groups && (grp < eg || (grp == eg && t < et)); ++grp, t = 0) {
     const int t0 = t, g_cur = grp;
-    dense_group<FMT, H, D, STORE, OUT>(p, grp * kRowsPerWave, wave, lane, [&](int trips) {
+    dense_group<FMT, H, D, STORE, OUT, EXACT>(p, grp * kRowsPerWave, wave, lane, [&](int trips) {
       const int units = max(trips, 1);
       const int t1 = g_cur < eg ? units : min(units, et);
       return GroupSeg{t0, t1, t0 == 0, t1 >= units};
@@ -290,55 +306,63 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_sched_kernel(DensePara
   }
 }
 
-template <int FMT, int H, int D, int STORE, int OUT, bool SCHED>
+template <int FMT, int H, int D, int STORE, int OUT, bool EXACT, bool SCHED>
 static hipError_t launch_dense_inst(const DenseParams& p, hipStream_t stream) {
   if constexpr (SCHED) {
     const int grid = (p.num_splits + kDenseWaves - 1) / kDenseWaves;
-    hipLaunchKernelGGL((dense_sched_kernel<FMT, H, D, STORE, OUT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((dense_sched_kernel<FMT, H, D, STORE, OUT, EXACT>), dim3((unsigned)grid),
                        dim3(kDenseThreads), 0, stream, p);
   } else {
     const int rblocks = (p.sq + kRowsPerWave * kDenseWaves - 1) / (kRowsPerWave * kDenseWaves);
     const int64_t grid = (int64_t)rblocks * p.n_chunks;
-    hipLaunchKernelGGL((dense_kernel<FMT, H, D, STORE, OUT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((dense_kernel<FMT, H, D, STORE, OUT, EXACT>), dim3((unsigned)grid),
                        dim3(kDenseThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int FMT, int H, int D, int OUT, bool SCHED>
-static hipError_t dispatch_store(const DenseParams& p, int store, hipStream_t s) {
+template <int FMT, int H, bool EXACT, int OUT, bool SCHED>
+static hipError_t dispatch_store(const DenseParams& p, int d, int store, hipStream_t s) {
+  if (d == 64) {
+    switch (store) {
+      case kDenseClean: return launch_dense_inst<FMT, H, 64, kDenseClean, OUT, EXACT, SCHED>(p, s);
+      case kDenseKeep: return launch_dense_inst<FMT, H, 64, kDenseKeep, OUT, EXACT, SCHED>(p, s);
+      default: return launch_dense_inst<FMT, H, 64, kCompressed, OUT, EXACT, SCHED>(p, s);
+    }
+  }
   switch (store) {
-    case kDenseClean: return launch_dense_inst<FMT, H, D, kDenseClean, OUT, SCHED>(p, s);
-    case kDenseKeep: return launch_dense_inst<FMT, H, D, kDenseKeep, OUT, SCHED>(p, s);
-    default: return launch_dense_inst<FMT, H, D, kCompressed, OUT, SCHED>(p, s);
+    case kDenseClean: return launch_dense_inst<FMT, H, 128, kDenseClean, OUT, EXACT, SCHED>(p, s);
+    case kDenseKeep: return launch_dense_inst<FMT, H, 128, kDenseKeep, OUT, EXACT, SCHED>(p, s);
+    default: return launch_dense_inst<FMT, H, 128, kCompressed, OUT, EXACT, SCHED>(p, s);
   }
 }
 
-template <int FMT, int H, int OUT, bool SCHED>
-static hipError_t dispatch_d(const DenseParams& p, int d, int store, hipStream_t s) {
-  return d == 64 ? dispatch_store<FMT, H, 64, OUT, SCHED>(p, store, s)
-                 : dispatch_store<FMT, H, 128, OUT, SCHED>(p, store, s);
-}
-
+// H <= 16 always runs EXACT (DenseMode); MXFP4 with H = 32 is the same code
+// either way (no split for fp4 products, no linear half).
 template <int FMT, int OUT, bool SCHED>
-static hipError_t dispatch_h(const DenseParams& p, int h, int d, int store, hipStream_t s) {
+static hipError_t dispatch_h(const DenseParams& p, int h, int d, int store, bool exact,
+                             hipStream_t s) {
   switch (h) {
-    case 8: return dispatch_d<FMT, 8, OUT, SCHED>(p, d, store, s);
-    case 16: return dispatch_d<FMT, 16, OUT, SCHED>(p, d, store, s);
-    case 32: return dispatch_d<FMT, 32, OUT, SCHED>(p, d, store, s);
-    default: return dispatch_d<FMT, 64, OUT, SCHED>(p, d, store, s);
+    case 8: return dispatch_store<FMT, 8, true, OUT, SCHED>(p, d, store, s);
+    case 16: return dispatch_store<FMT, 16, true, OUT, SCHED>(p, d, store, s);
+    case 32:
+      if (exact && FMT != kMXFP4) return dispatch_store<FMT, 32, true, OUT, SCHED>(p, d, store, s);
+      return dispatch_store<FMT, 32, false, OUT, SCHED>(p, d, store, s);
+    default:
+      if (exact) return dispatch_store<FMT, 64, true, OUT, SCHED>(p, d, store, s);
+      return dispatch_store<FMT, 64, false, OUT, SCHED>(p, d, store, s);
   }
 }
 
-// Every (format, H, D, store mode) instance with logits of type OUT, by row
-// chunks or (SCHED) by a work schedule.
+// Every (format, H, D, store mode, arithmetic) instance with logits of type
+// OUT, by row chunks or (SCHED) by a work schedule.
 template <int OUT, bool SCHED>
-static hipError_t dispatch_fmt(int fmt, int h, int d, int store, const DenseParams& p,
+static hipError_t dispatch_fmt(int fmt, int h, int d, int store, bool exact, const DenseParams& p,
                                hipStream_t s) {
   switch (fmt) {
-    case kFP8: return dispatch_h<kFP8, OUT, SCHED>(p, h, d, store, s);
-    case kMXFP8: return dispatch_h<kMXFP8, OUT, SCHED>(p, h, d, store, s);
-    default: return dispatch_h<kMXFP4, OUT, SCHED>(p, h, d, store, s);
+    case kFP8: return dispatch_h<kFP8, OUT, SCHED>(p, h, d, store, exact, s);
+    case kMXFP8: return dispatch_h<kMXFP8, OUT, SCHED>(p, h, d, store, exact, s);
+    default: return dispatch_h<kMXFP4, OUT, SCHED>(p, h, d, store, exact, s);
   }
 }
 

@@ -6,7 +6,7 @@ namespace mqa {
 
 hipError_t launch_dense_sched_bf16(int fmt, int h, int d, int store, const DenseParams& p,
                                    hipStream_t s) {
-  return dispatch_fmt<kBF16, true>(fmt, h, d, store, p, s);
+  return dispatch_fmt<kBF16, true>(fmt, h, d, store, p.exact != 0, p, s);
 }
 
 }  // namespace mqa

@@ -44,23 +44,12 @@ struct DenseParams {
   int32_t w_bf16;          // weights are bf16
   const int32_t* sched;    // [num_splits + 1][2] work schedule, or null (row chunks)
   int32_t num_splits;
-  const uint8_t* ql;       // [Sq, 4, D] e4m3 pieces of the weighted query sum (H = 64)
-  const uint8_t* ql_sf;    // [Sq, 4, D/32] their e8m0 scales
+  int32_t exact;           // every product exact (picks the instance; see Split)
 };
 
 // Heads whose kernels split ReLU into |x| / 2 and x / 2 and take the linear
-// half from the weighted query sum (qsum.hip).
+// half from the weighted query sum (RowGroup::make_lin).
 constexpr int kLinHeads = 64;
-
-struct QsumParams {
-  const uint8_t* q;        // [Sq, H, D] codes (fp4: D/2 bytes per row)
-  const uint8_t* q_sf;     // [Sq, H, D/32] or null
-  const void* w;           // [Sq, H] fp32 or bf16 (w_bf16)
-  uint8_t* ql;             // [Sq, 4, D]
-  uint8_t* ql_sf;          // [Sq, 4, D/32]
-  int32_t sq;
-  int32_t w_bf16;
-};
 
 struct PagedParams {
   const uint8_t* q;          // [batch*next_n, H, D]
@@ -77,6 +66,7 @@ struct PagedParams {
   int64_t stride;
   int32_t batch, next_n, bs, num_blocks, max_ctx, num_splits, nb_max;
   int32_t w_bf16;
+  int32_t exact;             // every product exact (picks the instance; see Split)
 };
 
 struct TopkParams {
@@ -100,7 +90,6 @@ hipError_t launch_dense_sched_bf16(int fmt, int h, int d, int store, const Dense
                                    hipStream_t s);
 hipError_t launch_dense_metadata(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
                                  int32_t num_splits, int32_t* sched, hipStream_t s);
-hipError_t launch_qsum(int fmt, int d, const QsumParams& p, hipStream_t s);
 hipError_t launch_compressed_offsets(const int32_t* ks, const int32_t* ke, int32_t sq, int32_t skv,
                                      int64_t* off, hipStream_t s);
 hipError_t launch_paged(int fmt, int h, int d, int clean, int out, const PagedParams& p,

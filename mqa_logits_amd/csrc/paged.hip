@@ -71,12 +71,15 @@ struct PairSink {
 // math -- walk the same blocks (the second read of a KV step comes from the
 // cache) and add their partial sums in PairSink.  Both waves take identical,
 // wave-uniform control flow, so they meet every barrier.
-template <int FMT, int H, int D, bool CLEAN, int OUT, int HS>
+//
+// EXACT: every product reaches the accumulator exactly (Split; always for
+// H <= 16, on request otherwise).
+template <int FMT, int H, int D, bool CLEAN, int OUT, int HS, bool EXACT>
 __global__ __launch_bounds__(kWaveLanes * HS, HS) void paged_kernel(PagedParams p) {
   static_assert(HS == 1 || (HS == 2 && CLEAN), "the head split writes clean logits only");
-  // Decode batches are small: the weighted-query-sum launch would cost more
-  // than the halved epilogue saves, so the paged kernel keeps max + fma.
-  using RG = RowGroup<FMT, H / HS, D>;
+  // The linear half of ReLU on the matrix core was measured not to pay off
+  // for decode batches, so the paged kernel keeps max + fma.
+  using RG = RowGroup<FMT, H / HS, D, false, EXACT || H <= 16>;
   using L = OperandLayout<FMT, D>;
   using OE = OutElem<OUT>;
   constexpr int kOB = OE::kBytes;              // bytes per logits element
@@ -265,34 +268,41 @@ __global__ __launch_bounds__(kWaveLanes * HS, HS) void paged_kernel(PagedParams 
 }
 
 // One block per worker: clean logits with 64 heads split the heads over two
-// waves, everything else runs one wave per worker.
-template <int FMT, int H, int D, int OUT>
+// waves (not EXACT: its eight KV operand copies want the registers the split
+// saves), everything else runs one wave per worker.
+template <int FMT, int H, int D, int OUT, bool EXACT>
 static hipError_t launch_paged_inst(int clean, const PagedParams& p, hipStream_t s) {
   const int grid = p.num_splits;
   if (clean) {
-    constexpr int kHS = H == 64 ? 2 : 1;
-    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true, OUT, kHS>), dim3(grid),
+    constexpr int kHS = (H == 64 && !EXACT) ? 2 : 1;
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, true, OUT, kHS, EXACT>), dim3(grid),
                        dim3(kWaveLanes * kHS), 0, s, p);
   } else {
-    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false, OUT, 1>), dim3(grid), dim3(kWaveLanes), 0,
-                       s, p);
+    hipLaunchKernelGGL((paged_kernel<FMT, H, D, false, OUT, 1, EXACT>), dim3(grid),
+                       dim3(kWaveLanes), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int FMT, int H, int OUT>
+template <int FMT, int H, int OUT, bool EXACT>
 static hipError_t paged_d(int d, int clean, const PagedParams& p, hipStream_t s) {
-  return d == 64 ? launch_paged_inst<FMT, H, 64, OUT>(clean, p, s)
-                 : launch_paged_inst<FMT, H, 128, OUT>(clean, p, s);
+  return d == 64 ? launch_paged_inst<FMT, H, 64, OUT, EXACT>(clean, p, s)
+                 : launch_paged_inst<FMT, H, 128, OUT, EXACT>(clean, p, s);
 }
 
+// H <= 16 always runs exact; MXFP4 products are exact without the split.
 template <int FMT, int OUT>
 static hipError_t paged_h(int h, int d, int clean, const PagedParams& p, hipStream_t s) {
+  const bool exact = p.exact != 0 && FMT != kMXFP4;
   switch (h) {
-    case 8: return paged_d<FMT, 8, OUT>(d, clean, p, s);
-    case 16: return paged_d<FMT, 16, OUT>(d, clean, p, s);
-    case 32: return paged_d<FMT, 32, OUT>(d, clean, p, s);
-    default: return paged_d<FMT, 64, OUT>(d, clean, p, s);
+    case 8: return paged_d<FMT, 8, OUT, true>(d, clean, p, s);
+    case 16: return paged_d<FMT, 16, OUT, true>(d, clean, p, s);
+    case 32:
+      return exact ? paged_d<FMT, 32, OUT, true>(d, clean, p, s)
+                   : paged_d<FMT, 32, OUT, false>(d, clean, p, s);
+    default:
+      return exact ? paged_d<FMT, 64, OUT, true>(d, clean, p, s)
+                   : paged_d<FMT, 64, OUT, false>(d, clean, p, s);
   }
 }
 

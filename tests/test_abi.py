@@ -51,12 +51,14 @@ def test_every_declared_symbol_is_exported():
 def dense_args(**kw):
     a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kv_scale=FAKE, w=FAKE,
              ks=FAKE, ke=FAKE, out=FAKE, stride=64, sq=16, skv=64, h=64, d=128, clean=1,
-             w_type=0, out_type=0, sched=None, splits=0, stream=None)
+             w_type=0, out_type=0, sched=None, splits=0, precision=0, stream=None)
     a.update(kw)
     return list(a.values())
 
 
 @pytest.mark.parametrize("change,expect", [
+    (dict(precision=2), INVALID),
+    (dict(precision=-1), INVALID),
     (dict(h=48), UNSUPPORTED),
     (dict(h=128), UNSUPPORTED),
     (dict(d=96), UNSUPPORTED),
@@ -92,12 +94,14 @@ def test_empty_problems_are_noops():
     assert lib.mqa_logits(*dense_args(sq=0)) == OK
     assert lib.mqa_logits(*dense_args(skv=0, stride=0)) == OK
     assert lib.mqa_logits_compressed(0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, 0, 64, 64, 128, 0, 0, None, 0, None) == OK
+                                     FAKE, FAKE, 0, 64, 64, 128, 0, 0, None, 0, 0, None) == OK
+    # the precision is checked even for an empty problem
+    assert lib.mqa_logits(*dense_args(sq=0, precision=3)) == INVALID
 
 
 def test_compressed_validation():
     base = [0, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 64, 128, 0, 0,
-            None, 0, None]
+            None, 0, 0, None]
     bad = list(base)
     bad[9] = None                                   # row_offsets
     assert lib.mqa_logits_compressed(*bad) == INVALID
@@ -106,6 +110,9 @@ def test_compressed_validation():
     assert lib.mqa_logits_compressed(*bad) == UNSUPPORTED
     bad = list(base)
     bad[16] = 5                                     # logits type
+    assert lib.mqa_logits_compressed(*bad) == INVALID
+    bad = list(base)
+    bad[19] = 9                                     # precision
     assert lib.mqa_logits_compressed(*bad) == INVALID
     assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, -1, 10, FAKE, None) == INVALID
     assert lib.mqa_logits_compressed_offsets(FAKE, FAKE, 4, 10, None, None) == INVALID
@@ -152,7 +159,7 @@ def paged_args(**kw):
     a = dict(dt=0, q=FAKE, q_sf=None, kv=FAKE, kv_sf=None, kvs=FAKE, w=FAKE, ctx=FAKE,
              bt=FAKE, bt_stride=512, sched=FAKE, out=FAKE, stride=32768, batch=64, next_n=4,
              h=64, d=128, bs=64, num_blocks=36000, max_ctx=32768, splits=1024, clean=1,
-             w_type=0, out_type=0, stream=None)
+             w_type=0, out_type=0, precision=0, stream=None)
     a.update(kw)
     return list(a.values())
 
@@ -168,6 +175,7 @@ def paged_args(**kw):
     (dict(kvs=None), INVALID),
     (dict(w_type=3), INVALID),
     (dict(out_type=1, stride=32769), INVALID),      # bf16 logits need an even stride
+    (dict(precision=5), INVALID),
 ])
 def test_paged_validation(change, expect):
     assert lib.paged_mqa_logits(*paged_args(**change)) == expect
