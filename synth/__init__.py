@@ -17,6 +17,10 @@ from .workloads import (  # noqa: F401
     pack_e2m1,
     dense_case,
     paged_case,
+    cancelling_dense_case,
+    cancelling_paged_case,
+    cancel_pairs,
+    CANCEL_BIG,
     config_case,
     CONFIG_NAMES,
     sampled_rows,

@@ -25,7 +25,7 @@ E4M3_MAX = 448.0
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 TENSOR_IDS = dict(q=0, kv=1, kv_scale=2, weights=3, context_lens=4, perm=5,
-                  q_sf=6, kv_sf=7, rows=8)
+                  q_sf=6, kv_sf=7, rows=8, pairs=10)
 
 
 def stream(seed, name):
@@ -232,6 +232,80 @@ def paged_case(batch, next_n, h, d, block_size, num_blocks, ctx_lo, ctx_hi,
     return PagedCase(fmt, batch, next_n, h, d, block_size, num_blocks, max_context_len,
                      q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
                      context_lens, block_table, seed, name)
+
+
+# --------------------------------------------------------------------------
+# cancelling dot products
+# --------------------------------------------------------------------------
+#
+# Inputs whose dots cancel: in every aligned group of 8 elements along D two
+# fixed positions carry +CANCEL_BIG and -CANCEL_BIG in Q and one equal value
+# in KV, so their products cancel exactly and the dot is the sum of the six
+# small products of each group.  Values are chosen so that every partial sum
+# of the products is a multiple of 2^-9 below 2^14 in magnitude (at most 23
+# significant bits): exact in fp32 in any order.
+#   Q: the pair, and smalls +-m * 2^-5 with m in {1, 1.125, .., 1.875};
+#   KV: +-1 or +-2 per element, the pair's two elements equal;
+#   MX: q block scales 2^-1 or 2^0, kv block scales 2^0 or 2^1.
+
+CANCEL_BIG = 128.0
+
+
+def cancel_pairs(seed, d):
+    """[D/8, 2]: the two positions of each group's cancelling pair."""
+    rng = stream(seed, "pairs")
+    return np.stack([rng.choice(8, 2, replace=False) for _ in range(d // 8)])
+
+
+def _cancel_q(rng, shape, pairs):
+    d = shape[-1]
+    x = rng.choice([-1.0, 1.0], size=shape) * (1.0 + rng.integers(0, 8, size=shape) / 8.0) / 32.0
+    g = np.arange(d // 8) * 8
+    x[..., g + pairs[:, 0]] = CANCEL_BIG
+    x[..., g + pairs[:, 1]] = -CANCEL_BIG
+    return encode_e4m3(x)
+
+
+def _cancel_kv(rng, shape, pairs):
+    d = shape[-1]
+    x = rng.choice([-2.0, -1.0, 1.0, 2.0], size=shape)
+    g = np.arange(d // 8) * 8
+    x[..., g + pairs[:, 1]] = x[..., g + pairs[:, 0]]
+    return encode_e4m3(x)
+
+
+def cancelling_dense_case(sq, skv, h, d, fmt="fp8", seed=0, k_start=None, k_end=None):
+    """dense_case with cancelling Q and KV codes (fp8 or mxfp8)."""
+    if fmt not in ("fp8", "mxfp8"):
+        raise ValueError(fmt)
+    case = dense_case(sq, skv, h, d, fmt, seed, k_start, k_end,
+                      name=f"cancelling_{fmt}_h{h}_d{d}")
+    pairs = cancel_pairs(seed, d)
+    case.q = _cancel_q(stream(seed, "q"), (sq, h, d), pairs)
+    case.kv = _cancel_kv(stream(seed, "kv"), (skv, d), pairs)
+    if fmt == "mxfp8":
+        case.q_sf = (126 + stream(seed, "q_sf").integers(0, 2, (sq, h, d // 32))).astype(np.uint8)
+        case.kv_sf = (127 + stream(seed, "kv_sf").integers(0, 2, (skv, d // 32))).astype(np.uint8)
+    return case
+
+
+def cancelling_paged_case(batch, next_n, h, d, block_size, num_blocks, ctx_lo, ctx_hi,
+                          max_context_len, fmt="fp8", seed=0):
+    """paged_case with cancelling Q and KV codes in the blocks it reads."""
+    if fmt not in ("fp8", "mxfp8"):
+        raise ValueError(fmt)
+    case = paged_case(batch, next_n, h, d, block_size, num_blocks, ctx_lo, ctx_hi,
+                      max_context_len, fmt, seed, name=f"cancelling_paged_{fmt}_h{h}_d{d}")
+    pairs = cancel_pairs(seed, d)
+    case.q = _cancel_q(stream(seed, "q"), case.q.shape, pairs)
+    n_used = -(-np.minimum(case.context_lens.astype(np.int64), max_context_len) // block_size)
+    used = np.unique(np.concatenate([case.block_table[b, :n_used[b]] for b in range(batch)]))
+    case.kv_pool[used] = _cancel_kv(stream(seed, "kv"), (used.size, block_size, d), pairs)
+    if fmt == "mxfp8":
+        case.q_sf = (126 + stream(seed, "q_sf").integers(0, 2, case.q_sf.shape)).astype(np.uint8)
+        case.kv_sf_pool[used] = (127 + stream(seed, "kv_sf").integers(
+            0, 2, (used.size, block_size, d // 32))).astype(np.uint8)
+    return case
 
 
 # --------------------------------------------------------------------------

@@ -85,3 +85,93 @@ def run_dense(case, clean=True, out=None):
     import mqa_logits_amd as mq
     return mq.mqa_logits(d["fmt"], d["q"], d["q_sf"], d["kv"], d["kv_sf"], d["kv_scale"],
                          d["weights"], d["k_start"], d["k_end"], clean_logits=clean, out=out)
+
+
+# ---------------------------------------------------------------------------
+# The error class of the default precision (matrix-core grouped summation)
+# ---------------------------------------------------------------------------
+#
+# In MQA_PRECISION_DEFAULT every aligned group of 8 fp8 products along D is
+# summed after each product is truncated toward zero to a multiple of
+# 2^(E - 13), E the exponent of the group's largest product (measured on the
+# device).  The error of one dot is then below 7 * 2^(E - 13) per group <=
+# 2^-10.19 * sum_d |q_d kv_d|, so with S = sum_h |w_h s_j| sum_d |q_hd kv_jd|
+# the weighted head sum is off by less than about 2^-10.1 * S.  With H = 64 the
+# linear half of ReLU comes from q' = sum_h (w_h / 2) q_h rounded to four e4m3
+# pieces per 32-element block, which keeps about 16 bits below the block's
+# largest |q'|: that adds at most 2^-15 * |s_j| sum_b max_{d in b} |q'_d|
+# sum_{d in b} |kv_jd|.  The class bound below doubles the first term.
+
+def default_class_bound(fmt, Q, K, kvs, w, lin):
+    """Q [r, H, D], K [c, D] decoded (block scales applied), kvs [c], w [r, H]
+    -> extra tolerance [r, c] of the default precision on top of the literal
+    bound."""
+    S = np.einsum("rh,rhc->rc", np.abs(w), np.abs(Q) @ np.abs(K).T) * np.abs(kvs)[None, :]
+    extra = 2.0 ** -9 * S
+    if lin:
+        qp = np.einsum("rh,rhd->rd", w / 2.0, Q)                 # [r, D]
+        nb = Q.shape[-1] // 32
+        m = np.abs(qp).reshape(qp.shape[0], nb, 32).max(-1)      # [r, nb]
+        ksum = np.abs(K).reshape(K.shape[0], nb, 32).sum(-1)     # [c, nb]
+        extra = extra + 2.0 ** -15 * (m @ ksum.T) * np.abs(kvs)[None, :]
+    return extra
+
+
+def dense_class_bound(case, lin):
+    Q = oracle.codecs.decode(case.fmt, case.q, case.q_sf)
+    K = oracle.codecs.decode(case.fmt, case.kv, case.kv_sf)
+    kvs = (np.ones(case.skv) if case.kv_scale is None
+           else case.kv_scale.astype(np.float64))
+    return default_class_bound(case.fmt, Q, K, kvs, case.weights.astype(np.float64), lin)
+
+
+# ---------------------------------------------------------------------------
+# Full rows of the large workloads: the oracle over row blocks on a thread
+# pool (numpy releases the GIL in its matrix products and ufuncs), BLAS held
+# to one thread per worker; each block is compared as it arrives.
+# ---------------------------------------------------------------------------
+
+def oracle_workers():
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def assert_rows_close(got_rows, case, rows, what, row_block=4):
+    """got_rows: float32 [len(rows), Skv] from the GPU; rows: their indices.
+    Runs oracle.dense_logits on blocks of row_block rows in parallel and checks
+    every entry (mask bit-exact, values within the bound).  Returns the
+    largest |gpu - ref| / bound."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    rows = np.asarray(rows, dtype=np.int64)
+    starts = list(range(0, rows.size, row_block))
+
+    def one(b0):
+        r = rows[b0:b0 + row_block]
+        ref, bound = oracle.dense_logits(*case.args(), rows=r, row_block=row_block)
+        g = np.asarray(got_rows[b0:b0 + r.size], dtype=np.float64)
+        inf_ref = np.isneginf(ref)
+        if not np.array_equal(np.isneginf(g), inf_ref):
+            bad = np.argwhere(np.isneginf(g) != inf_ref)[:3]
+            return ("mask", int(r[0]), bad.tolist())
+        fin = ~inf_ref
+        if not np.isfinite(g[fin]).all():
+            return ("nonfinite", int(r[0]), None)
+        if not fin.any():
+            return ("ok", 0.0, None)
+        ratio = np.abs(g[fin] - ref[fin]) / bound[fin]
+        return ("ok", float(ratio.max()), None)
+
+    worst = 0.0
+    with threadpool_limits(limits=1), ThreadPoolExecutor(oracle_workers()) as ex:
+        for kind, val, extra in ex.map(one, starts):
+            assert kind != "mask", f"{what}: -inf mask differs in the block at row {val}: {extra}"
+            assert kind != "nonfinite", f"{what}: non-finite value in range near row {val}"
+            worst = max(worst, val)
+    log(f"   {what}: {rows.size} full rows, max |gpu-ref|/bound = {worst:.3g}")
+    assert worst <= 1.0, f"{what}: |gpu-ref|/bound = {worst:.3g}"
+    return worst

@@ -1,16 +1,15 @@
 """GPU parity of the large MX workload (Sq=8192, Skv=65536, H=64, D=128) in
-MXFP8 and MXFP4: full -inf mask on the device, complete sampled rows, and
-4096 sampled rows at sampled columns (the oracle computes those entries one by
-one).  The 2 GiB output stays on the device.
+MXFP8 and MXFP4: the full -inf mask on the device, then 4096 sampled rows
+(always rows 0 and Sq-1) compared in full with the oracle.  The 2 GiB output
+stays on the device; the sampled rows come back in slices.
 """
 
 import numpy as np
 import pytest
 import torch
 
-import oracle
 import synth
-from tests.gpu_helpers import assert_close, assert_mask_on_device, log, run_dense
+from tests.gpu_helpers import assert_mask_on_device, assert_rows_close, log, run_dense
 
 pytestmark = pytest.mark.gpu
 
@@ -23,22 +22,14 @@ def _device():
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-def test_config4_mx_large(fmt):
+def test_config4_mx_large_4096_full_rows(fmt):
     case = synth.config_case(4, fmt)
     log(f"[mx] config 4 {fmt}")
     out = run_dense(case)
     torch.cuda.synchronize()
     assert_mask_on_device(out, case.k_start, case.k_end, case.skv, rows_per_chunk=64)
-    rows = synth.sampled_rows(case.seed, case.sq, 8)
-    ref, bound = oracle.dense_logits(*case.args(), rows=rows, row_block=2)
-    assert_close(out[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, bound, f"c4_{fmt}_rows")
-    srows = synth.sampled_rows(case.seed, case.sq, 4096)
-    rng = np.random.default_rng(case.seed)
-    r = np.repeat(srows, 4)
-    c = rng.integers(0, case.skv, r.size)
-    c[::4] = np.maximum(0, case.k_end[srows] - 1)
-    v, b = oracle.dense_entries(*case.args(), r, c)
-    got = out[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()].cpu().numpy()
-    assert_close(got, v, b, f"c4_{fmt}_entries")
+    rows = synth.sampled_rows(case.seed, case.sq, 4096)
+    got = out[torch.from_numpy(rows).cuda()].cpu().numpy()       # 1 GiB of fp32
     del out
     torch.cuda.empty_cache()
+    assert_rows_close(got, case, rows, f"c4_{fmt}", row_block=2)

@@ -308,3 +308,51 @@ def test_paged_mx_equals_dense_on_gathered_kv():
         d_ref, _ = oracle.dense_logits("mxfp4", case.q[rows], case.q_sf[rows], kv, sf, None,
                                        case.weights[rows], np.zeros(2), ctx - 2 + np.arange(2) + 1)
         assert np.array_equal(ref[rows, :ctx], d_ref)
+
+
+def test_hand_worked_paged_example():
+    """Two sequences through a permuted block table, block_size 4, next_n 2,
+    H = 2, D = 2; sequence 1's context (9) exceeds max_context_len (7), so its
+    rows see only the first 7 tokens.  Every expected value below was worked
+    out by hand from the definition (query token t of sequence b is row
+    b*next_n + t and covers keys [0, ctx_b - next_n + t + 1) clamped to
+    min(ctx_b, max_context_len); logical token j is slot j % 4 of physical
+    block block_table[b, j // 4]).  Physical block 2 is never read and holds
+    NaN codes and a NaN scale."""
+    nan8 = 0x7F
+    kv_vals = {0: [[1, 0], [0, 1], [1, 1], [2, 0]],
+               1: [[0, 2], [1, -1], [-1, 1], [2, 2]],
+               3: [[1, 2], [2, 1], [-1, 0], [0, -1]],
+               4: [[3, 0], [0, 3], [1, -2], [-2, 1]]}
+    kv_pool = np.full((5, 4, 2), nan8, np.uint8)
+    for blk, v in kv_vals.items():
+        kv_pool[blk] = encode_e4m3(np.array(v, np.float32))
+    kvs_pool = np.array([[1, 1, 2, 0.5], [1, 2, 1, 1], [np.nan] * 4, [1, 0.5, 1, 2],
+                         [2, 1, 1, 0.5]], np.float32)
+    block_table = np.array([[3, 0], [4, 1]], np.int32)
+    q = encode_e4m3(np.array([[[1, 0], [0, 1]],        # row 0 = (b 0, t 0)
+                              [[1, 1], [-1, 1]],       # row 1 = (b 0, t 1)
+                              [[1, -1], [2, 0]],       # row 2 = (b 1, t 0)
+                              [[0, 1], [1, 1]]],       # row 3 = (b 1, t 1)
+                             np.float32))
+    w = np.array([[1, 2], [0.5, 1], [1, -1], [2, 0.5]], np.float32)
+    ctx = np.array([6, 9], np.int32)
+
+    # the gather alone: sequence 1's 7 visible tokens, in logical order
+    kv1, s1 = oracle.gather_paged_kv(kv_pool, kvs_pool, block_table, 1, 7, 4)
+    assert np.array_equal(kv1, encode_e4m3(np.array(
+        [[3, 0], [0, 3], [1, -2], [-2, 1], [0, 2], [1, -1], [-1, 1]], np.float32)))
+    assert np.array_equal(s1, np.array([2, 1, 1, 0.5, 1, 2, 1], np.float32))
+    # the row ranges, with the clamp at max_context_len
+    _, e = oracle.paged_row_ranges(ctx, 2, 7)
+    assert e.tolist() == [5, 6, 7, 7]
+
+    ninf = -np.inf
+    expected = np.array([[5, 2, 0, 0, 1, ninf, ninf],
+                         [2.5, 0.75, 1, 0, 0.5, 1.5, ninf],
+                         [-6, 0, 1, 0, 0, 0, 0],
+                         [3, 7.5, 0, 1, 5, 0, 2]])
+    ref, bound = oracle.paged_logits("fp8", q, None, kv_pool, None, kvs_pool, w, ctx,
+                                     block_table, 2, 4, 7)
+    assert np.array_equal(ref, expected)
+    assert np.all(bound[np.isneginf(expected)] == 0)

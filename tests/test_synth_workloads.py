@@ -47,3 +47,22 @@ def test_config3_shape_in_mx_formats(fmt):
     # the same sequences and block table as config 3
     assert np.array_equal(case.context_lens, ref.context_lens)
     assert np.array_equal(case.block_table, ref.block_table)
+
+
+@pytest.mark.parametrize("fmt,d", [("fp8", 128), ("mxfp8", 64)])
+def test_cancelling_case_properties(fmt, d):
+    """The cancelling inputs hold what their description promises: the pair
+    products cancel exactly in every group of 8, and every product is a
+    multiple of 2^-9 with sum |products| < 2^14 (partial sums exact in fp32)."""
+    from oracle.codecs import decode
+    import synth
+    case = synth.cancelling_dense_case(6, 50, 32, d, fmt, seed=5)
+    Q = decode(fmt, case.q, case.q_sf)                 # [6, 32, d]
+    K = decode(fmt, case.kv, case.kv_sf)               # [50, d]
+    P = Q[:, :, None, :] * K[None, None, :, :]
+    assert np.all(np.mod(P * 512.0, 1.0) == 0)
+    assert np.abs(P).sum(-1).max() < 2.0 ** 14
+    pairs = synth.cancel_pairs(5, d)
+    g = np.arange(d // 8) * 8
+    assert np.all(P[..., g + pairs[:, 0]] + P[..., g + pairs[:, 1]] == 0)
+    assert np.all(np.abs(Q[..., g + pairs[:, 0]]) >= 64)
