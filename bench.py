@@ -7,12 +7,19 @@ full call of the path on inputs already resident in HBM.  Metric: effective
 TFLOP/s = 2 * H * D * (in-range entries) / time; masked and -inf entries are
 not counted.
 
-Prints one JSON line.  Other workloads (--workload) are for measurement notes.
+Order of work (all on cuda:0, one JSON line on stdout):
+  1. inputs, one call and the full -inf mask check;
+  2. cold window: the next 20 calls, timed together (reported, not the value);
+  3. graph replay: 5 calls with distinct outputs captured in one HIP graph,
+     5 replays, then 40 samples of an untimed replay followed by an
+     event-timed one; median, p10 and p90 per call (reported);
+  4. W warmup steps, then exactly K steps between a barrier-free pair of HIP
+     events, with host wall time around them: `value` is the effective
+     TFLOP/s over the wall time, `roofline.achieved` over the event time;
+  5. the MFMA microbenchmark (rate and the clock its waves ran at), and the
+     CPU oracle on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1]
-
-Without --warmup the warmup runs for at least 150 ms (the clocks settle);
-the JSON line reports the number of warmup steps taken.
 """
 
 import argparse
@@ -79,52 +86,6 @@ def measured_traffic(workload):
         return None
 
 
-class SclkSampler:
-    """Samples the current shader clock from sysfs (pp_dpm_sclk, the line
-    marked '*') in a background thread; mean() is None where unreadable."""
-
-    def __init__(self, period_s=0.002):
-        import glob
-        import threading
-        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-        self.path = paths[0] if paths else None
-        self.samples = []
-        self.period = period_s
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _read(self):
-        try:
-            with open(self.path) as f:
-                for line in f:
-                    if line.rstrip().endswith("*"):
-                        return float(line.split(":")[1].strip().rstrip("*").strip().lower()
-                                     .replace("mhz", ""))
-        except (OSError, ValueError, IndexError):
-            return None
-        return None
-
-    def _run(self):
-        while not self._stop.is_set():
-            v = self._read()
-            if v is not None:
-                self.samples.append(v)
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        if self.path:
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self.path:
-            self._thread.join()
-
-    def mean(self):
-        return float(np.mean(self.samples)) if self.samples else None
-
-
 def mfma_microbench():
     """Dense fp8 MFMA rate and shader clock from libmqa_peak.so (one wave per
     SIMD, chains of the same MFMA the kernels use); None if unavailable."""
@@ -169,12 +130,15 @@ def check_mask(out, case, rows_per_chunk=128):
             raise SystemExit(f"mask check failed in rows [{r0}, {r1})")
 
 
-def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
-    """Returns (step_fn, info dict) with inputs resident on cuda:0.
+def build_step(name, schedule=False, logits_dtype="fp32", zero=False, precision="default"):
+    """Returns (step_fn, info) with inputs resident on cuda:0.
 
-    schedule: dense / compressed calls follow a work schedule made by
-    mqa_logits_metadata once, outside the steps (its own time is reported as
-    metadata_ms).  logits_dtype: fp32 or bf16 logits."""
+    info["call"](o) makes one full call of the path writing into output buffer
+    o; info["outs"] are distinct output buffers (5, or 2 for the 2 GiB
+    outputs); step() calls into them in turn.  schedule: dense / compressed
+    calls follow a work schedule made by mqa_logits_metadata once, outside the
+    steps (its own time is reported as metadata_ms).  logits_dtype: fp32 or
+    bf16 logits."""
     import torch
     import mqa_logits_amd as mq
     import synth
@@ -187,6 +151,15 @@ def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
     case = synth.config_case(idx, fmt, zero=zero)
     dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
     info = dict(workload=case.name + ("_zero" if zero else ""), case=case)
+    n_out = 2 if idx == 4 else 5
+
+    def rotating(call, outs):
+        state = {"i": 0}
+
+        def step():
+            call(outs[state["i"] % len(outs)])
+            state["i"] += 1
+        return step
 
     def dense_schedule(ks, ke):
         if not schedule:
@@ -208,28 +181,24 @@ def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
         d = [dev(x) for x in case.args()[1:]]
         q, q_sf, kv, kv_sf, kvs, w, ks, ke = d
         sched, extra = dense_schedule(ks, ke)
-        n_out = 2 if idx == 4 else 4          # distinct output buffers, rotated
         outs = [mq._logits_rows(case.sq, case.skv, out_dtype, "cuda") for _ in range(n_out)]
-        state = {"i": 0}
 
-        def step():
-            o = outs[state["i"] % n_out]
-            state["i"] += 1
-            mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o, schedule=sched)
+        def call(o):
+            mq.mqa_logits(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke, out=o, schedule=sched,
+                          precision=precision)
         nvalid = valid_entries_dense(case)
         info["topk"] = lambda k: time_topk(lambda: mq.mqa_logits_topk(outs[0], k, ks, ke),
                                            nvalid * out_size + case.sq * k * 4)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
-                    out_bytes=float(out_size) * case.sq * case.skv,
-                    sq=case.sq, skv=case.skv, h=case.h, d=case.d, outs=outs,
+                    out_bytes=float(out_size) * case.sq * case.skv, call=call, outs=outs,
                     cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
                              format=case.fmt, layout="dense", clean_logits=True,
                              logits=logits_dtype, schedule=bool(schedule)), **extra)
         # mask check before timing (the pages' reproducer checks the mask too)
-        step()
+        call(outs[0])
         torch.cuda.synchronize()
         check_mask(outs[0], case)
-        return step, info
+        return rotating(call, outs), info
 
     if idx == 2:
         d = [dev(x) for x in case.args()[1:]]
@@ -237,22 +206,20 @@ def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
         off = mq.mqa_logits_compressed_offsets(ks, ke, case.skv)
         total = int(off[-1].item())
         sched, extra = dense_schedule(ks, ke)
-        outs = [torch.empty(total, dtype=out_dtype, device="cuda") for _ in range(4)]
-        state = {"i": 0}
+        outs = [torch.empty(total, dtype=out_dtype, device="cuda") for _ in range(n_out)]
 
-        def step():
-            o = outs[state["i"] % 4]
-            state["i"] += 1
+        def call(o):
             mq.mqa_logits_compressed_offsets(ks, ke, case.skv, out=off)
             mq.mqa_logits_compressed(case.fmt, q, q_sf, kv, kv_sf, kvs, w, ks, ke,
-                                     row_offsets=off, out=o, schedule=sched)
+                                     row_offsets=off, out=o, schedule=sched,
+                                     precision=precision)
         nvalid = valid_entries_dense(case)
         info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="mfma",
-                    out_bytes=float(out_size) * total,
+                    out_bytes=float(out_size) * total, call=call, outs=outs,
                     cfg=dict(sq=case.sq, skv=case.skv, heads=case.h, head_dim=case.d,
                              format=case.fmt, layout="compressed", logits=logits_dtype,
                              schedule=bool(schedule)), **extra)
-        return step, info
+        return rotating(call, outs), info
 
     # paged decode
     pd = dict(q=dev(case.q), q_sf=dev(case.q_sf), kv=dev(case.kv_pool),
@@ -262,17 +229,14 @@ def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
     sched = mq.paged_mqa_logits_metadata(pd["ctx"], case.next_n, case.block_size,
                                          case.max_context_len, splits)
     rows = case.batch * case.next_n
-    outs = [mq._logits_rows(rows, case.max_context_len, out_dtype, "cuda") for _ in range(4)]
-    state = {"i": 0}
+    outs = [mq._logits_rows(rows, case.max_context_len, out_dtype, "cuda") for _ in range(n_out)]
 
     # The schedule is made once per decoding step and shared by every layer's
     # kernel: it is timed on its own, outside the steps.
-    def step():
-        o = outs[state["i"] % 4]
-        state["i"] += 1
+    def call(o):
         mq.paged_mqa_logits(case.fmt, pd["q"], pd["q_sf"], pd["kv"], pd["kv_sf"], pd["kvs"],
                             pd["w"], pd["ctx"], pd["bt"], sched, case.next_n,
-                            case.max_context_len, out=o)
+                            case.max_context_len, out=o, precision=precision)
 
     def metadata_ms(n=50):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -297,10 +261,43 @@ def build_step(name, schedule=False, logits_dtype="fp32", zero=False):
     info.update(flops=2.0 * case.h * case.d * nvalid, fmt=case.fmt, bound="hbm",
                 out_bytes=out_bytes, extra=lambda: {"metadata_ms": metadata_ms()},
                 bytes=kv_bytes + out_bytes + case.q.nbytes + case.weights.nbytes,
+                call=call, outs=outs,
                 cfg=dict(batch=case.batch, next_n=case.next_n, heads=case.h, head_dim=case.d,
                          block_size=case.block_size, max_context_len=case.max_context_len,
                          format=case.fmt, layout="paged", splits=splits, logits=logits_dtype))
-    return step, info
+    return rotating(call, outs), info
+
+
+def graph_protocol(call, outs, samples=40):
+    """The pages' timing method: 3 warm-up calls; one HIP graph holding one
+    call per distinct output buffer; 5 replays; then `samples` times an
+    untimed replay followed by an event-timed one.  Returns per-call median,
+    p10 and p90 in ms."""
+    import statistics
+    import torch
+    for _ in range(3):
+        call(outs[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for o in outs:
+            call(o)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(samples):
+        g.replay()
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / len(outs))
+    srt = sorted(times)
+    return {"calls_per_graph": len(outs), "samples": samples,
+            "median_ms": statistics.median(times), "p10_ms": srt[int(0.1 * (samples - 1))],
+            "p90_ms": srt[int(0.9 * (samples - 1))]}
 
 
 def time_topk(fn, nbytes, n=50):
@@ -322,12 +319,17 @@ def time_topk(fn, nbytes, n=50):
 
 
 def cpu_baseline(info, seconds):
-    """The oracle, as it stands, on leading rows of the same workload."""
+    """The oracle, as it stands, on leading rows of the same workload for about
+    `seconds` of wall time with every BLAS thread the process has; plus the
+    extrapolated time of the whole workload and, for scale, the whole tiny
+    workload (256 x 1024, H 16, D 64) on one thread."""
     import oracle                          # the oracle is used by this leg only
+    import synth
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     case = info["case"]
     if not hasattr(case, "sq"):
@@ -341,24 +343,33 @@ def cpu_baseline(info, seconds):
         flops += 2.0 * case.h * case.d * float((e[rows] - s[rows]).sum())
         done = rows[-1] + 1
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{done - 1} of the same workload (float64 numpy oracle), "
-                      f"{dt:.1f} s wall"}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"rows 0..{done - 1} of the same workload (float64 numpy oracle), "
+                     f"{dt:.1f} s wall",
+           "rows_per_s": done / dt,
+           "extrapolated_full_workload_s": dt * info["flops"] / flops if flops else None}
+    if threadpool_limits is not None:
+        tiny = synth.config_case(0)
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            oracle.dense_logits(*tiny.args())
+            out["tiny_workload_one_thread_s"] = time.perf_counter() - t1
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU raises its clocks only after tens of milliseconds of sustained
-    # load: without --warmup, warm up for at least 150 ms (and 20 steps).
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay protocol")
     ap.add_argument("--schedule", action="store_true",
                     help="dense/compressed calls follow an mqa_logits_metadata work schedule")
     ap.add_argument("--logits-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--precision", default="default", choices=["default", "exact"])
     ap.add_argument("--zero", action="store_true",
                     help="all-zero Q, KV and weights with unit scales (the pages' timing "
                          "workload; dense workloads only)")
@@ -378,49 +389,51 @@ def main():
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range((args.warmup or 0) + args.steps):
+        for _ in range(args.warmup + args.steps):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n,
-                          "launches": (args.warmup or 0) + args.steps}), flush=True)
+                          "launches": args.warmup + args.steps}), flush=True)
         return
-    step, info = build_step(args.workload, args.schedule, args.logits_dtype, args.zero)
+    step, info = build_step(args.workload, args.schedule, args.logits_dtype, args.zero,
+                            args.precision)
     if args.zero:
         info["cfg"]["inputs"] = "all_zero"
-    if args.warmup is not None:
-        for _ in range(args.warmup):
-            step()
-    else:
-        args.warmup = 0
-        t_w = time.perf_counter()
-        while args.warmup < 20 or time.perf_counter() - t_w < 0.15:
-            step()
-            args.warmup += 1
-            if args.warmup % 10 == 0:
-                torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    # timed region: K back-to-back steps between two HIP events on the launch
-    # stream (an event per step would put a cache-flushing marker between the
-    # launches and time that too)
+    if args.precision != "default":
+        info["cfg"]["precision"] = args.precision
+    flops = info["flops"]
     stream = torch.cuda.current_stream()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with SclkSampler() as sclk:
+
+    def timed(n):
+        """n back-to-back steps between two HIP events on the launch stream;
+        (host wall s, event ms per step)."""
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         a.record(stream)
-        for _ in range(args.steps):
+        for _ in range(n):
             step()
         b.record(stream)
-        torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = a.elapsed_time(b) / args.steps
+        b.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, a.elapsed_time(b) / n
 
-    flops = info["flops"]
+    # cold window: the first calls after setup (the shader clock dips for
+    # tens of milliseconds once sustained load starts)
+    _, cold_ms = timed(20)
+    graph = None if args.no_graph else graph_protocol(info["call"], info["outs"])
+
+    for _ in range(args.warmup):
+        step()
+    # timed region (an event per step would put a cache-flushing marker between
+    # the launches and time that too)
+    wall, per_launch_ms = timed(args.steps)
+
     value = flops * args.steps / wall / 1e12
-    # the committed counter summaries cover the default call (fp32 logits, no schedule)
-    default_call = not args.schedule and args.logits_dtype == "fp32"
+    # the committed counter summaries cover the default call
+    default_call = (not args.schedule and args.logits_dtype == "fp32"
+                    and args.precision == "default" and not args.zero)
     traffic = measured_traffic(args.workload) if default_call else None
     if info["bound"] == "mfma":
         achieved = flops / (per_launch_ms * 1e-3) / 1e12
@@ -444,7 +457,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_ms": per_launch_ms,
-        "sclk_mhz_during_timing": sclk.mean(),
+        "cold_window": {"calls": 20, "ms_per_call": cold_ms,
+                        "frac": (flops / (cold_ms * 1e-3) / 1e12 / PEAK_TFLOPS[info["fmt"]]
+                                 if info["bound"] == "mfma" else None)},
+        "graph_replay": graph,
         "mfma_microbench": peak_probe,
         "hbm_write_gbs": info["out_bytes"] / (per_launch_ms * 1e-3) / 1e9,
     }
