@@ -135,6 +135,13 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;      // gfx9 raw 32-bit buffer
 constexpr int kOOB = 0x7ff00000;           // every range stays below this
 constexpr int kNT = 2;                           // non-temporal cache hint
 
+// kOOB when `drop` (a wave-uniform condition), else 0, to OR into a byte
+// offset: offsets stay below kOOB, so off | oob_if(drop) is off or an offset
+// the range check drops.  Arithmetic rather than a select: a select on a
+// uniform condition compiles to a branch around the store, which splits a
+// walk's loop into blocks that the scheduler cannot interleave across.
+__device__ __forceinline__ int oob_if(bool drop) { return -(int)drop & kOOB; }
+
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
@@ -224,6 +231,7 @@ struct LinLds {
 template <int FMT, int H, int D, bool LIN = false, bool EXACT = false>
 struct RowGroup {
   static_assert(!(LIN && EXACT), "the linear half rounds q' to e4m3 pieces");
+  static constexpr int kTokens = kTileN;                    // tokens per step
   static constexpr int kMT = H / 4;
   static constexpr int kNKB = D / 32;                       // e8m0 blocks per row
   static constexpr int kRowBytes = OperandLayout<FMT, D>::kRowBytes;  // bytes per row
@@ -542,46 +550,59 @@ struct KvOp {
 // counting the loads issued after them, and that count is fixed once for the
 // loop's first and later trips alike, so a first step issued last would make
 // every trip wait for all loads in flight.
-template <class Load>
+template <int NT = kTileN, class Load>
 __device__ __forceinline__ void prefetch_span(int cl, KvOp (&o)[kKvStages], Load&& load) {
 #pragma unroll
   for (int u = 0; u < kKvStages - 1; ++u) {
-    load(cl + u * kTileN, o[u]);
+    load(cl + u * NT, o[u]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// A step's finished value(s) times the token scale |s|, kept ahead of the
+// store that follows: one row per lane (float) or two (float2).
+__device__ __forceinline__ float scale_vals(float v, float s) {
+  v *= s;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ float2 scale_vals(float2 v, float s) {
+  v.x *= s;
+  v.y *= s;
+  asm volatile("" : "+v"(v.x), "+v"(v.y));
+  return v;
+}
+
+// RG::kTokens tokens per step (16, or 32 for the D = 64 tiles of tile32.hpp).
 template <bool FLIP, class RG, class Load, class Sink>
 __device__ __forceinline__ int compute_span(RG& rg, int cl, int ch, KvOp (&o)[kKvStages],
                                             Load&& load, Sink& sink) {
   constexpr int S = kKvStages;
-  const int steps = (ch - cl + kTileN - 1) / kTileN;
-  const int end = cl + (steps + S - 1) / S * S * kTileN;
-  o[S - 1].ks = 0.f;                           // the phantom step cl - 16
+  constexpr int NT = RG::kTokens;
+  const int steps = (ch - cl + NT - 1) / NT;
+  const int end = cl + (steps + S - 1) / S * S * NT;
+  o[S - 1].ks = 0.f;                           // the phantom step cl - NT
   rg.start();
 
-  for (int j0 = cl; j0 < end; j0 += S * kTileN) {
+  for (int j0 = cl; j0 < end; j0 += S * NT) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
-      KvOp& cur = o[u];                        // step j0 + 16 u
-      KvOp& prv = o[(u + S - 1) % S];          // step j0 + 16 (u - 1), finished in this one
+      KvOp& cur = o[u];                        // step j0 + NT u
+      KvOp& prv = o[(u + S - 1) % S];          // step j0 + NT (u - 1), finished in this one
       if constexpr (FLIP) cur.b = negate_fp8(cur.b, cur.ks < 0.f ? (int)0x80808080 : 0);
-      rg.step(cur.b, cur.bs, [&](float v) {
-        v *= __builtin_fabsf(prv.ks);
-        asm volatile("" : "+v"(v));            // keep the reduction ahead of the store
-        sink.put((u + S - 1) % S, j0 + (u - 1) * kTileN, v);
+      rg.step(cur.b, cur.bs, [&](auto v) {
+        sink.put((u + S - 1) % S, j0 + (u - 1) * NT, scale_vals(v, __builtin_fabsf(prv.ks)));
       });
-      if (u == 0) sink.trip(j0 - S * kTileN);
-      load(j0 + (u - 1 + S) * kTileN, prv);
+      if (u == 0) sink.trip(j0 - S * NT);
+      load(j0 + (u - 1 + S) * NT, prv);
       // keep the refill here: sunk towards its use it would leave a single
       // step to cover the load latency
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  float v = rg.drain() * __builtin_fabsf(o[S - 1].ks);   // the last step sits in slot S - 1
-  asm volatile("" : "+v"(v));
-  sink.put(S - 1, end - kTileN, v);
-  sink.trip(end - S * kTileN);
+  // the last step sits in slot S - 1
+  sink.put(S - 1, end - NT, scale_vals(rg.drain(), __builtin_fabsf(o[S - 1].ks)));
+  sink.trip(end - S * NT);
   sink.finish();
   return end;
 }
@@ -594,8 +615,7 @@ struct DwordSink {
   OffFn off;                                   // (j0, &v) -> byte offset or kOOB; may edit v
   int lo_j0;                                   // steps below lo_j0 are dropped
   __device__ __forceinline__ void put(int, int j0, float v) {
-    int o = off(j0, v);
-    o = j0 >= lo_j0 ? o : kOOB;
+    const int o = off(j0, v) | oob_if(j0 < lo_j0);
     OutElem<OUT>::store1(r, o, v);
   }
   __device__ __forceinline__ void trip(int) {}
@@ -604,6 +624,25 @@ struct DwordSink {
 
 constexpr int kTripCols = kTileN * kKvStages;  // columns per pipeline trip
 static_assert(kTripCols == 64, "StagedSink::buffer() divides by 64");
+
+// The part of a 4-row group's work one wave does.  The group's computed
+// range (the union of its rows' ranges, from a trip-aligned start) is
+// `trips` trips of kTripCols columns; the wave computes trips [t_a, t_b) of it
+// and writes the output columns around them: from column 0 if `first`, up to
+// Skv if `last`.  The pieces of a group partition its rows.
+struct GroupSeg {
+  int t_a, t_b;
+  bool first, last;
+};
+
+// Trips of a 4-row group's computed range: the union [lo, hi) of its
+// non-empty rows' clamped ranges, from lo rounded down to a trip boundary
+// (0 when every row is empty).  The dense work split counts these.
+__device__ __forceinline__ int group_trips(int lo, int hi) {
+  if (lo >= hi) return 0;
+  const int lo64 = lo & ~(kTripCols - 1);
+  return (hi - lo64 + kTripCols - 1) / kTripCols;
+}
 
 // Clean output.  A trip's 4 rows x kTripCols columns are staged in LDS (as
 // fp32) and leave as one 4-column store per lane (lane l: row l / 16,
@@ -638,7 +677,7 @@ struct StagedSink {
   __device__ __forceinline__ void trip(int jt) {
     asm volatile("" ::: "memory");            // the group read follows every lane's writes
     pend = *reinterpret_cast<const float4*>(buffer(jt) + rd_idx);
-    pend_off = (jt >= base && jt <= last_j0) ? row_off + OutElem<OUT>::kBytes * jt : kOOB;
+    pend_off = (jt <= last_j0 ? row_off + OutElem<OUT>::kBytes * jt : kOOB) | oob_if(jt < base);
     asm volatile("" ::: "memory");
   }
   __device__ __forceinline__ void finish() { OutElem<OUT>::store4(r, pend_off, pend); }

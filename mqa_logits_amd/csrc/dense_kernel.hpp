@@ -23,29 +23,11 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile32.hpp"
 
 namespace mqa {
 
 constexpr int kDenseThreads = kWaveLanes * kDenseWaves;
-
-// The part of a 4-row group's work one wave does.  The group's computed
-// range (the union of its rows' ranges, from a trip-aligned start) is
-// `trips` trips of kTripCols columns; the wave computes trips [t_a, t_b) of it
-// and writes the output columns around them: from column 0 if `first`, up to
-// Skv if `last`.  The pieces of a group partition its rows.
-struct GroupSeg {
-  int t_a, t_b;
-  bool first, last;
-};
-
-// Trips of a 4-row group's computed range: the union [lo, hi) of its
-// non-empty rows' clamped ranges, from lo rounded down to a trip boundary
-// (0 when every row is empty).  The dense work split counts these.
-__device__ __forceinline__ int group_trips(int lo, int hi) {
-  if (lo >= hi) return 0;
-  const int lo64 = lo & ~(kTripCols - 1);
-  return (hi - lo64 + kTripCols - 1) / kTripCols;
-}
 
 // Arithmetic of an instance: EXACT splits the KV operand so that every
 // product reaches the accumulator exactly (always for H <= 16, whose few
@@ -272,11 +254,13 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) 
   const int chunk = bid - rblock * p.n_chunks;
   const int row0 = (rblock * kDenseWaves + wave) * kRowsPerWave;
   if (row0 >= p.sq) return;
-  dense_group<FMT, H, D, STORE, OUT, EXACT>(p, row0, wave, lane, [&](int trips) {
+  auto seg = [&](int trips) {
     return GroupSeg{(int)((int64_t)chunk * trips / p.n_chunks),
                     (int)((int64_t)(chunk + 1) * trips / p.n_chunks), chunk == 0,
                     chunk == p.n_chunks - 1};
-  });
+  };
+  if constexpr (D == 64) dense_group32<FMT, STORE, OUT, EXACT, H>(p, row0, wave, lane, seg);
+  else dense_group<FMT, H, D, STORE, OUT, EXACT>(p, row0, wave, lane, seg);
 }
 
 // Scheduled: wave w of block b is worker kDenseWaves * b + w and walks its
@@ -298,11 +282,13 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_sched_kernel(DensePara
   const int et = max(p.sched[2 * worker + 3], 0);
   for (; grp < n_groups && (grp < eg || (grp == eg && t < et)); ++grp, t = 0) {
     const int t0 = t, g_cur = grp;
-    dense_group<FMT, H, D, STORE, OUT, EXACT>(p, grp * kRowsPerWave, wave, lane, [&](int trips) {
+    auto seg = [&](int trips) {
       const int units = max(trips, 1);
       const int t1 = g_cur < eg ? units : min(units, et);
       return GroupSeg{t0, t1, t0 == 0, t1 >= units};
-    });
+    };
+    if constexpr (D == 64) dense_group32<FMT, STORE, OUT, EXACT, H>(p, grp * kRowsPerWave, wave, lane, seg);
+    else dense_group<FMT, H, D, STORE, OUT, EXACT>(p, grp * kRowsPerWave, wave, lane, seg);
   }
 }
 
@@ -337,8 +323,7 @@ static hipError_t dispatch_store(const DenseParams& p, int d, int store, hipStre
   }
 }
 
-// H <= 16 always runs EXACT (DenseMode); MXFP4 with H = 32 is the same code
-// either way (no split for fp4 products, no linear half).
+// H <= 16 always runs EXACT (DenseMode, DenseMode32).
 template <int FMT, int OUT, bool SCHED>
 static hipError_t dispatch_h(const DenseParams& p, int h, int d, int store, bool exact,
                              hipStream_t s) {
@@ -346,7 +331,7 @@ static hipError_t dispatch_h(const DenseParams& p, int h, int d, int store, bool
     case 8: return dispatch_store<FMT, 8, true, OUT, SCHED>(p, d, store, s);
     case 16: return dispatch_store<FMT, 16, true, OUT, SCHED>(p, d, store, s);
     case 32:
-      if (exact && FMT != kMXFP4) return dispatch_store<FMT, 32, true, OUT, SCHED>(p, d, store, s);
+      if (exact) return dispatch_store<FMT, 32, true, OUT, SCHED>(p, d, store, s);
       return dispatch_store<FMT, 32, false, OUT, SCHED>(p, d, store, s);
     default:
       if (exact) return dispatch_store<FMT, 64, true, OUT, SCHED>(p, d, store, s);

@@ -58,7 +58,7 @@ struct PairSink {
     const float4 a = *reinterpret_cast<const float4*>(mine + half(jt) + rd_idx);
     const float4 b = *reinterpret_cast<const float4*>(other + half(jt) + rd_idx);
     pend = float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
-    pend_off = (jt >= base && jt <= last_j0) ? row_off + OutElem<OUT>::kBytes * jt : kOOB;
+    pend_off = (jt <= last_j0 ? row_off + OutElem<OUT>::kBytes * jt : kOOB) | oob_if(jt < base);
     asm volatile("" ::: "memory");
   }
   __device__ __forceinline__ void finish() { OutElem<OUT>::store4(r, pend_off, pend); }
