@@ -80,11 +80,12 @@ mqa_status check_common(mqa_dtype dt, const void* q, const uint8_t* q_sf, const 
   return MQA_OK;
 }
 
-// Chunks per row group: about one wave per SIMD (a single dispatch round, one
-// prologue per SIMD; the chunks of a row group carry equal work), with runs
-// of at least one 64-token trip (few rows: more, shorter chunks).
-int32_t pick_chunks(int32_t sq, int32_t skv) {
-  constexpr int64_t kTargetBlocks = 1024 / mqa::kDenseWaves;
+// Chunks per row group: about as many waves as the SIMDs hold at once (a
+// single dispatch round, one prologue per wave; the chunks of a row group
+// carry equal work), with runs of at least one 64-token trip (few rows: more,
+// shorter chunks).
+int32_t pick_chunks(int32_t sq, int32_t skv, int32_t waves_per_simd) {
+  const int64_t kTargetBlocks = 1024 * waves_per_simd / mqa::kDenseWaves;
   const int64_t qblocks = (sq + 4 * mqa::kDenseWaves - 1) / (4 * mqa::kDenseWaves);
   int64_t n_chunks = (kTargetBlocks + qblocks - 1) / qblocks;
   const int64_t max_chunks = (skv + 63) / 64;
@@ -139,7 +140,7 @@ mqa_status run_dense(mqa_dtype dt, const void* q, const uint8_t* q_sf, const voi
   p.stride = stride;
   p.sq = sq;
   p.skv = skv;
-  p.n_chunks = pick_chunks(sq, skv);
+  p.n_chunks = pick_chunks(sq, skv, mqa::dense_waves_per_simd((int)dt, d));
   p.w_bf16 = weights_type == MQA_BF16;
   p.sched = schedule;
   p.num_splits = schedule ? num_splits : 0;

@@ -237,11 +237,23 @@ struct RowGroup {
   static constexpr int kRowBytes = OperandLayout<FMT, D>::kRowBytes;  // bytes per row
   static constexpr int kWays = Split<FMT, EXACT>::kWays;
 
-  v8i qa[kMT];                                              // tile m
+  // Tile m's A operand.  e2m1 rows fill only dwords 0..3 (OperandLayout);
+  // the matrix core reads four registers for them, so only those are held.
+  static constexpr int kQDwords = FMT == kMXFP4 ? 4 : 8;
+  typedef int qop_t __attribute__((ext_vector_type(kQDwords)));
+  qop_t qa[kMT];
   int qs[kMT];
   float w[H];
   v8i ql;                                                   // LIN: the q' pieces
   int qls;
+
+  __device__ __forceinline__ v8i a_op(int m) const {
+    if constexpr (kQDwords == 8) {
+      return qa[m];
+    } else {
+      return v8i{qa[m][0], qa[m][1], qa[m][2], qa[m][3], 0, 0, 0, 0};
+    }
+  }
 
   // a_row(r) = the query row that A row r (0..3 -> lanes' (l>>2)&3) reads;
   // e_row = the query row whose outputs this lane accumulates (lane >> 4).
@@ -262,7 +274,11 @@ struct RowGroup {
       const uint8_t* row = q + hr * L::kRowBytes;
       const uint4 a = lo >= 0 ? *reinterpret_cast<const uint4*>(row + lo) : zero4();
       const uint4 b = hi >= 0 ? *reinterpret_cast<const uint4*>(row + hi) : zero4();
-      qa[m] = make_op(a, b);
+      if constexpr (kQDwords == 8) {
+        qa[m] = make_op(a, b);
+      } else {
+        qa[m] = qop_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+      }
       if constexpr (FmtInfo<FMT>::kMX) {
         qs[m] = L::scale_ok(g) ? (int)q_sf[hr * L::kBlocks + g] : 127;
       } else {
@@ -502,9 +518,9 @@ struct RowGroup {
 #pragma unroll
     for (int m = 0; m < kMT; ++m) {
       reduce_tile((m - kLag + kMT) % kMT, acc[(m - kLag + kRing) % kRing]);
-      v4f c = mma<FMT>(qa[m], bp[0], qs[m], scale_b);
+      v4f c = mma<FMT>(a_op(m), bp[0], qs[m], scale_b);
 #pragma unroll
-      for (int k = 1; k < kWays; ++k) c = mma<FMT>(qa[m], bp[k], qs[m], scale_b, c);
+      for (int k = 1; k < kWays; ++k) c = mma<FMT>(a_op(m), bp[k], qs[m], scale_b, c);
       acc[m % kRing] = c;
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerTile, 0);   // the reduction VALU
       __builtin_amdgcn_sched_group_barrier(0x008, kWays, 0);          // then the tile's MFMAs

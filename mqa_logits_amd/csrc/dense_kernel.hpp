@@ -241,7 +241,7 @@ __device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int 
 // the union of a group's ranges splits into n_chunks runs of whole trips of
 // nearly equal length, so the chunks of a group do the same MFMA work.
 template <int FMT, int H, int D, int STORE, int OUT, bool EXACT>
-__global__ __launch_bounds__(kDenseThreads, 1) void dense_kernel(DenseParams p) {
+__global__ __launch_bounds__(kDenseThreads, dense_waves_per_simd(FMT, D)) void dense_kernel(DenseParams p) {
   const int lane = threadIdx.x & (kWaveLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Blocks are dispatched round-robin over the 8 XCDs; renumber them so each

@@ -22,6 +22,11 @@ constexpr int kWavesPerBlock = 1;
 constexpr int kDenseWaves = 4;
 // Resident waves per compute unit the kernels are sized for (one per SIMD).
 constexpr int kWavesPerCu = 4;
+// Waves per SIMD the chunked dense kernel is built for: two for e2m1 elements
+// with D = 128 (their Q operands take half the registers, and a second wave's
+// epilogue can run beside a 4-pass fp4 MFMA), one otherwise.  The scheduled
+// kernel keeps one (its worker count is the caller's).
+constexpr int dense_waves_per_simd(int fmt, int d) { return fmt == 2 && d == 128 ? 2 : 1; }
 // KV operand buffers in flight per wave: a step's operands are requested
 // kKvStages - 1 steps (16 tokens each) before their MFMAs issue, and a wave
 // walks whole trips of kKvStages steps.
