@@ -537,10 +537,14 @@ struct RowGroup {
 };
 
 // One streamed KV operand: the MFMA B operand of a 16-token step, its e8m0
-// scale (MX) and its fp32 token scale (FP8).
+// scale (MX) and its fp32 token scale (FP8).  The e8m0 byte is held as a
+// byte: widened where a step uses it, the widening waits only for that step's
+// loads.  Held widened, the ring's values would be widened at the top of the
+// walk's loop body, which waits for every slot's scale load, the last
+// refill's included.
 struct KvOp {
   v8i b;
-  int bs;
+  uint8_t bs;
   float ks;
 };
 

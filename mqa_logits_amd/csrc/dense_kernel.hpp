@@ -147,7 +147,7 @@ __device__ __forceinline__ void dense_group(const DenseParams& p, int row0, int 
   auto load_b = [&](int j0, KvOp& o) {
     o.b = buffer_operand(kv_r, b_lo, b_hi, j0 * kRowBytes);
     if constexpr (FmtInfo<FMT>::kMX) {
-      o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, sc_lane, j0 * kNKB, 0) : 127;
+      o.bs = kb_ok ? __builtin_amdgcn_raw_buffer_load_b8(sc_r, sc_lane, j0 * kNKB, 0) : (uint8_t)127;
       o.ks = 1.f;
     } else {
       o.bs = 127;

@@ -200,8 +200,10 @@ __global__ __launch_bounds__(kWaveLanes * HS, HS) void paged_kernel(PagedParams 
           const Rsrc kv_r = make_rsrc(p.kv + (int64_t)tok * kRowBytes, kTileN * kRowBytes);
           o.b = buffer_operand(kv_r, b_lo, b_hi);
           if constexpr (FmtInfo<FMT>::kMX) {
-            o.bs = kb_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, (tok + n) * kNKB + kb, 0, 0)
-                         : 127;
+            // lanes past the row's scale blocks (D = 64) read 0 past the
+            // buffer's end: their operand pieces are zero, so any finite
+            // scale serves, and the load needs no branch
+            o.bs = __builtin_amdgcn_raw_buffer_load_b8(sc_r, kb_ok ? (tok + n) * kNKB + kb : kOOB, 0, 0);
             o.ks = 1.f;
           } else {
             o.bs = 127;

@@ -517,7 +517,7 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
   auto load_b = [&](int j0, KvOp& o) {
     o.b = buffer_operand(kv_r, b_lo, b_hi, j0 * kRowBytes);
     if constexpr (FmtInfo<FMT>::kMX) {
-      o.bs = (int)__builtin_amdgcn_raw_buffer_load_b8(sc_r, sc_lane, j0 * L::kBlocks, 0);
+      o.bs = __builtin_amdgcn_raw_buffer_load_b8(sc_r, sc_lane, j0 * L::kBlocks, 0);
       o.ks = 1.f;
     } else {
       o.bs = 127;
