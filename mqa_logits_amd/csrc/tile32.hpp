@@ -88,10 +88,12 @@ struct RowGroup32 {
     return 16 * (m % kHG) + 4 * ((lane >> 3) & 3) + (lane & 3);
   }
 
+  // Issues the loads of the Q operands, their block scales and the weights;
+  // finish() then forms the linear-half operand and pins the operands.
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
                                        const uint8_t* __restrict__ q_sf,
                                        const void* __restrict__ wts, bool w_bf16, int row0, int sq,
-                                       int lane, char* lin_lds) {
+                                       int lane) {
     const int g = lane >> 5;
 #pragma unroll
     for (int m = 0; m < kMT; ++m) {
@@ -108,10 +110,6 @@ struct RowGroup32 {
       }
       qa[m] = make_op(a, b);
     }
-    if constexpr (LIN) make_lin(q_sf, wts, w_bf16, row0, sq, lane, lin_lds);
-#pragma unroll
-    for (int m = 0; m < kMT; ++m) asm volatile("" : "+a"(qa[m]));
-    if constexpr (LIN) asm volatile("" : "+a"(ql));
     constexpr float kW = LIN ? 0.5f : 1.f;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -139,6 +137,18 @@ struct RowGroup32 {
         }
       }
     }
+  }
+
+  // The Q operands stay resident for the whole walk and are only read by the
+  // MFMAs, which take A from AGPRs: pin them there (LIN: after forming the
+  // linear-half operand from them).
+  __device__ __forceinline__ void finish(const uint8_t* __restrict__ q_sf,
+                                         const void* __restrict__ wts, bool w_bf16, int row0,
+                                         int sq, int lane, char* lin_lds) {
+    if constexpr (LIN) make_lin(q_sf, wts, w_bf16, row0, sq, lane, lin_lds);
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) asm volatile("" : "+a"(qa[m]));
+    if constexpr (LIN) asm volatile("" : "+a"(ql));
   }
 
   // LIN: the linear-half operand (RowGroup::make_lin's arithmetic in this
@@ -459,8 +469,6 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
     __shared__ __attribute__((aligned(16))) char lin_all[kDenseWaves][LinLds32::kBytes];
     lin_lds = lin_all[wave];
   }
-  rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, row0, p.sq, lane, lin_lds);
-  __builtin_amdgcn_sched_barrier(0);
 
   int s_r[kRowsPerWave], e_r[kRowsPerWave];
   int lo = 0x7fffffff, hi = 0;
@@ -486,18 +494,6 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
   if (cl >= ch) { cl = c1; ch = c1; }
   const int lenA = max(0, min(eA, c1) - sA), relA = n - sA;
   const int lenB = max(0, min(eB, c1) - sB), relB = n - sB;
-
-  Rsrc out_r;
-  char* const out_base = static_cast<char*>(p.out);
-  int64_t first = 0;
-  if constexpr (STORE == kCompressed) {
-    first = uniform64(p.row_off[row0]);
-    const int64_t last = uniform64(p.row_off[min(row0 + kRowsPerWave, p.sq)]);
-    out_r = make_rsrc(out_base + first * kOB, (uint32_t)((last - first) * kOB));
-  } else {
-    const int rows = min(kRowsPerWave, p.sq - row0);
-    out_r = make_rsrc(out_base + (int64_t)row0 * p.stride * kOB, (uint32_t)(rows * p.stride * kOB));
-  }
 
   // KV operand of lane l: token j0 + l % 32, lane group l / 32's pieces and
   // block scale.
@@ -525,25 +521,59 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
     }
   };
 
+  // The walk's first operands, the first round of the scale scan below and
+  // the Q operands go out back to back, so their latencies overlap: the
+  // prologue waits for memory once.
   KvOp ring[kKvStages];
   if (cl < ch) prefetch_span<32>(cl, ring, load_b);
 
+  // For FP8, whether any token scale of the span is negative (the FLIP walk
+  // then negates those tokens' codes; ReLU(s x) = |s| ReLU(sign(s) x)):
+  // 16-byte loads, kPer in flight per lane, zero past the array.
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  constexpr int kPer = 8;
+  constexpr int kScanRound = 4 * kPer * kWaveLanes;          // columns per round
+  v4i sv[kPer];
+  if constexpr (!FmtInfo<FMT>::kMX) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b128(sc_r, 4 * (cl + 4 * lane + 4 * kWaveLanes * u), 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, row0, p.sq, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
   bool flip = false;
   if constexpr (!FmtInfo<FMT>::kMX) {
-    if (cl < ch) {
-      typedef int v4i __attribute__((ext_vector_type(4)));
-      constexpr int kPer = 32;
-      int neg = 0;
-      for (int j = cl + 4 * lane; j < ch; j += 4 * kPer * kWaveLanes) {
-        v4i sv[kPer];
+    int neg = 0;
 #pragma unroll
-        for (int u = 0; u < kPer; ++u)
-          sv[u] = __builtin_amdgcn_raw_buffer_load_b128(sc_r, 4 * (j + 4 * kWaveLanes * u), 0, 0);
+    for (int u = 0; u < kPer; ++u) neg |= (sv[u][0] | sv[u][1]) | (sv[u][2] | sv[u][3]);
+    for (int j = cl + kScanRound + 4 * lane; j < ch; j += kScanRound) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) neg |= (sv[u][0] | sv[u][1]) | (sv[u][2] | sv[u][3]);
-      }
-      flip = __ballot(neg < 0) != 0;
+      for (int u = 0; u < kPer; ++u)
+        sv[u] = __builtin_amdgcn_raw_buffer_load_b128(sc_r, 4 * (j + 4 * kWaveLanes * u), 0, 0);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) neg |= (sv[u][0] | sv[u][1]) | (sv[u][2] | sv[u][3]);
     }
+    // any sign bit set (-0.0 is harmless; scales past the span only cost the
+    // exact path)
+    flip = cl < ch && __ballot(neg < 0) != 0;
+  }
+
+  rg.finish(p.q_sf, p.w, p.w_bf16 != 0, row0, p.sq, lane, lin_lds);
+  __builtin_amdgcn_sched_barrier(0);
+
+  Rsrc out_r;
+  char* const out_base = static_cast<char*>(p.out);
+  int64_t first = 0;
+  if constexpr (STORE == kCompressed) {
+    first = uniform64(p.row_off[row0]);
+    const int64_t last = uniform64(p.row_off[min(row0 + kRowsPerWave, p.sq)]);
+    out_r = make_rsrc(out_base + first * kOB, (uint32_t)((last - first) * kOB));
+  } else {
+    const int rows = min(kRowsPerWave, p.sq - row0);
+    out_r = make_rsrc(out_base + (int64_t)row0 * p.stride * kOB, (uint32_t)(rows * p.stride * kOB));
   }
 
   auto walk = [&](auto& sink) {
