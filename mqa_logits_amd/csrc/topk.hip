@@ -31,14 +31,6 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWaveLanes;
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;       // key of -inf: not a candidate
 
-// x, hidden from value-range reasoning.  The ordered writes cap a count at
-// need_eq with min(); LLVM has been seen to drop such a min (a wrong result,
-// caught by the tests), so the cap goes through this.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // Order-preserving key of an fp32 bit pattern: larger float, larger key.
 __device__ __forceinline__ uint32_t order_key(uint32_t bits) {
   return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
@@ -301,7 +293,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
     for (int u = 0; u < 4; ++u) {
       const int i = 4 * t + u;
       if (i < n_b && kk[u] > K) {
-        const uint32_t pos = gb + min(qb, opaque(need_eq));
+        const uint32_t pos = gb + min(qb, need_eq);
         if (pos < (uint32_t)kTopkCap) chosen[pos] = cc[u];
         ++gb;
       } else if (i < n_b && kk[u] == K) {
@@ -362,7 +354,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
     for (int u = 0; u < 4; ++u) {
       const bool valid = kk[u] != kKeyNegInf;
       if (valid && kk[u] > K) {
-        const uint32_t pos = gb + min(qb, opaque(need_eq));
+        const uint32_t pos = gb + min(qb, need_eq);
         if (pos < (uint32_t)p.topk) out[pos] = s + c + u;
         ++gb;
       } else if (valid && kk[u] == K) {
@@ -552,8 +544,14 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
 #pragma unroll
   for (int j = 0; j < kWpt; ++j) {
     // the == K columns of this word still taken: the lowest `take` set bits
+    // the == K columns placed before this word, and how many of this word's
+    // are taken.  Written without a guarded subtraction: as
+    // `qb < need_eq ? min(need_eq - qb, nq) : 0`, LLVM evaluated the
+    // subtraction unconditionally with its no-wrap flag and then folded
+    // min(qb, need_eq) below to qb, a wrong position when qb > need_eq.
     const uint32_t nq = __popc(wq[j]);
-    uint32_t take = qb < need_eq ? min(need_eq - qb, nq) : 0u;
+    const uint32_t placed = min(qb, need_eq);
+    uint32_t take = min(need_eq - placed, nq);
     uint32_t sel_q = 0, rest = wq[j];
     for (; take > 0; --take) {
       const uint32_t low = rest & (0u - rest);
@@ -561,7 +559,7 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
       rest ^= low;
     }
     uint32_t word = wg[j] | sel_q;
-    uint32_t pos = gb + min(qb, opaque(need_eq));   // == K columns placed before this word
+    uint32_t pos = gb + placed;
     const int col0 = s + 32 * (t * kWpt + j);
     while (word) {
       const int b = __builtin_ctz(word);
