@@ -148,7 +148,7 @@ def build_step(name, schedule=False, logits_dtype="fp32", zero=False, precision=
 
     idx = WORKLOADS[name]
     fmt = name.split("-")[1] if "-" in name else None
-    case = synth.config_case(idx, fmt, zero=zero)
+    case = synth.workload_case(idx, fmt, zero=zero)
     dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
     info = dict(workload=case.name + ("_zero" if zero else ""), case=case)
     n_out = 2 if idx == 4 else 5
@@ -349,7 +349,7 @@ def cpu_baseline(info, seconds):
            "rows_per_s": done / dt,
            "extrapolated_full_workload_s": dt * info["flops"] / flops if flops else None}
     if threadpool_limits is not None:
-        tiny = synth.config_case(0)
+        tiny = synth.workload_case(0)
         with threadpool_limits(limits=1):
             t1 = time.perf_counter()
             oracle.dense_logits(*tiny.args())

@@ -21,8 +21,8 @@ from .workloads import (  # noqa: F401
     cancelling_paged_case,
     cancel_pairs,
     CANCEL_BIG,
-    config_case,
-    CONFIG_NAMES,
+    workload_case,
+    WORKLOAD_NAMES,
     sampled_rows,
     topk_logits,
 )

@@ -312,7 +312,7 @@ def cancelling_paged_case(batch, next_n, h, d, block_size, num_blocks, ctx_lo, c
 # the five named workloads
 # --------------------------------------------------------------------------
 
-CONFIG_NAMES = {
+WORKLOAD_NAMES = {
     0: "dense_tiny_sq256_skv1024_h16_d64_fp8",
     1: "dense_prefill_sq2048_skv32768_h64_d128_fp8",
     2: "compressed_sq2048_skv4096_h32_d64_fp8",
@@ -321,7 +321,7 @@ CONFIG_NAMES = {
 }
 
 
-def config_case(idx, fmt=None, zero=False):
+def workload_case(idx, fmt=None, zero=False):
     """The five workloads, seeded with 1000 + idx.  idx 4 takes fmt
     'mxfp8' (default) or 'mxfp4'; idx 1 and 3 take 'fp8' (default), 'mxfp8'
     or 'mxfp4' (idx 1: the shape the pages time their MX kernels on).  zero: the dense
@@ -333,26 +333,26 @@ def config_case(idx, fmt=None, zero=False):
     if idx == 0:
         sq, skv = 256, 1024
         return dense_case(sq, skv, 16, 64, "fp8", seed, k_end=skv - sq + np.arange(sq) + 1,
-                          zero=zero, name=CONFIG_NAMES[0])
+                          zero=zero, name=WORKLOAD_NAMES[0])
     if idx == 1:
         fmt = fmt or "fp8"
         sq, skv = 2048, 32768
-        name = CONFIG_NAMES[1] if fmt == "fp8" else CONFIG_NAMES[1].replace("_fp8", "_" + fmt)
+        name = WORKLOAD_NAMES[1] if fmt == "fp8" else WORKLOAD_NAMES[1].replace("_fp8", "_" + fmt)
         return dense_case(sq, skv, 64, 128, fmt, seed, k_end=skv - sq + np.arange(sq),
                           zero=zero, name=name)
     if idx == 2:
         sq, skv = 2048, 4096
         return dense_case(sq, skv, 32, 64, "fp8", seed, k_start=np.arange(sq),
-                          k_end=np.full(sq, skv), zero=zero, name=CONFIG_NAMES[2])
+                          k_end=np.full(sq, skv), zero=zero, name=WORKLOAD_NAMES[2])
     if idx == 3:
         fmt = fmt or "fp8"
-        name = CONFIG_NAMES[3] if fmt == "fp8" else CONFIG_NAMES[3].replace("_fp8", "_" + fmt)
+        name = WORKLOAD_NAMES[3] if fmt == "fp8" else WORKLOAD_NAMES[3].replace("_fp8", "_" + fmt)
         return paged_case(64, 4, 64, 128, 64, 36000, 1024, 32768, 32768, fmt, seed, name=name)
     if idx == 4:
         fmt = fmt or "mxfp8"
         sq, skv = 8192, 65536
         return dense_case(sq, skv, 64, 128, fmt, seed, k_end=skv - sq + np.arange(sq),
-                          zero=zero, name=CONFIG_NAMES[4] + "_" + fmt)
+                          zero=zero, name=WORKLOAD_NAMES[4] + "_" + fmt)
     raise ValueError(idx)
 
 

@@ -3,7 +3,7 @@
 Every test runs the HIP path through the C ABI (mqa_logits_amd) on seeded
 inputs from synth and compares element by element with oracle/ (see
 gpu_helpers for the rules).  Sizes span several 16x16 tiles, several column
-chunks and ragged tails; config 1's full-size workload is checked on every
+chunks and ragged tails; the 2048x32768 prefill workload is checked on every
 row and column, after a full mask check on the device.
 """
 
@@ -35,8 +35,8 @@ def _check_dense(case, clean=True, what=""):
     return assert_close(out.cpu().numpy(), ref, bound, what or case.name, clean=clean)
 
 
-def test_config0_tiny_full_parity():
-    _check_dense(synth.config_case(0))
+def test_tiny_256x1024_full_parity():
+    _check_dense(synth.workload_case(0))
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
@@ -133,17 +133,17 @@ def test_bitwise_determinism_20_repeats():
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
-def test_config1_prefill_every_row(fmt):
-    # fp8 is config 1; the MX formats run its shape (two column chunks per
-    # row group, where config 4 takes one).  Every row, every column.
-    case = synth.config_case(1, fmt)
-    log(f"[dense] config 1 full size, {fmt}, every row")
+def test_prefill_2048x32768_every_row(fmt):
+    # fp8 is the prefill workload; the MX formats run its shape (two column
+    # chunks per row group, where the 8192x65536 workload takes one).  Every row, every column.
+    case = synth.workload_case(1, fmt)
+    log(f"[dense] prefill 2048x32768, {fmt}, every row")
     out = run_dense(case)
     torch.cuda.synchronize()
     assert_mask_on_device(out, case.k_start, case.k_end, case.skv)
     got = out.cpu().numpy()
     del out
-    assert_rows_close(got, case, np.arange(case.sq), f"config1_{fmt}", row_block=4)
+    assert_rows_close(got, case, np.arange(case.sq), f"prefill_{fmt}", row_block=4)
 
 
 # ---------------------------------------------------------------------------
@@ -163,8 +163,8 @@ def _check_compressed(case, what):
     assert_close(packed.cpu().numpy(), ref, bound, what)
 
 
-def test_config2_compressed_full_parity():
-    _check_compressed(synth.config_case(2), "config2")
+def test_compressed_2048x4096_full_parity():
+    _check_compressed(synth.workload_case(2), "compressed")
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])

@@ -22,9 +22,9 @@ def _device():
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-def test_config4_mx_large_4096_full_rows(fmt):
-    case = synth.config_case(4, fmt)
-    log(f"[mx] config 4 {fmt}")
+def test_mx_8192x65536_4096_full_rows(fmt):
+    case = synth.workload_case(4, fmt)
+    log(f"[mx] 8192x65536 {fmt}")
     out = run_dense(case)
     torch.cuda.synchronize()
     assert_mask_on_device(out, case.k_start, case.k_end, case.skv, rows_per_chunk=64)

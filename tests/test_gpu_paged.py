@@ -130,21 +130,21 @@ def test_paged_negative_scales_and_keep_mode():
     assert_close(np.where(inside, got, -np.inf), ref, bound, "paged_keep")
 
 
-def test_config3_paged_decode_full_parity_and_split_independence():
-    case = synth.config_case(3)
+def test_paged_decode_64x4_full_parity_and_split_independence():
+    case = synth.workload_case(3)
     import mqa_logits_amd as mq
     splits = mq.paged_mqa_logits_default_splits(0)
-    out = _check(case, splits, "config3")
-    log("[paged] config 3 with other split counts")
+    out = _check(case, splits, "paged_decode")
+    log("[paged] decode workload with other split counts")
     for other in (97, 2 * splits):
         out2, _ = _run(case, other)
         assert torch.equal(out.view(torch.int32), out2.view(torch.int32)), f"splits={other}"
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-def test_config3_shape_in_mx_formats_full_parity(fmt):
+def test_paged_decode_shape_in_mx_formats_full_parity(fmt):
     # the paged decode workload at full size in the MX formats (the two-wave
     # head split with e8m0 block scales), every row against the oracle
-    case = synth.config_case(3, fmt)
+    case = synth.workload_case(3, fmt)
     import mqa_logits_amd as mq
-    _check(case, mq.paged_mqa_logits_default_splits(0), f"config3_{fmt}")
+    _check(case, mq.paged_mqa_logits_default_splits(0), f"paged_decode_{fmt}")

@@ -1,4 +1,4 @@
-"""The workload generators' variants (host only): config 1's shape in the MX
+"""The workload generators' variants (host only): the prefill shape in the MX
 formats and the all-zero inputs the source pages time their kernels on."""
 
 import numpy as np
@@ -8,43 +8,43 @@ import synth
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-def test_config1_shape_in_mx_formats(fmt):
-    case = synth.config_case(1, fmt)
+def test_prefill_shape_in_mx_formats(fmt):
+    case = synth.workload_case(1, fmt)
     assert (case.sq, case.skv, case.h, case.d, case.fmt) == (2048, 32768, 64, 128, fmt)
     assert case.name.endswith("_" + fmt)
     assert case.kv_scale is None and case.q_sf is not None and case.kv_sf is not None
     assert case.q.shape[-1] == (128 if fmt == "mxfp8" else 64)
-    # the rows are config 1's: [0, Skv - Sq + i)
+    # the rows are the prefill workload's: [0, Skv - Sq + i)
     assert np.array_equal(case.k_end, 32768 - 2048 + np.arange(2048))
 
 
-def test_default_configs_keep_their_names():
-    assert synth.config_case(1).name == synth.CONFIG_NAMES[1]
-    assert synth.config_case(0).name == synth.CONFIG_NAMES[0]
+def test_default_workloads_keep_their_names():
+    assert synth.workload_case(1).name == synth.WORKLOAD_NAMES[1]
+    assert synth.workload_case(0).name == synth.WORKLOAD_NAMES[0]
 
 
 @pytest.mark.parametrize("idx,fmt", [(0, None), (1, None), (1, "mxfp4"), (2, None)])
 def test_all_zero_variant(idx, fmt):
-    case = synth.config_case(idx, fmt, zero=True)
+    case = synth.workload_case(idx, fmt, zero=True)
     assert not case.q.any() and not case.kv.any() and not case.weights.any()
     if case.q_sf is not None:
         assert (case.q_sf == 127).all() and (case.kv_sf == 127).all()   # unit e8m0 scales
-    ref = synth.config_case(idx, fmt)
+    ref = synth.workload_case(idx, fmt)
     assert np.array_equal(case.k_start, ref.k_start) and np.array_equal(case.k_end, ref.k_end)
 
 
 def test_paged_has_no_all_zero_variant():
     with pytest.raises(ValueError):
-        synth.config_case(3, zero=True)
+        synth.workload_case(3, zero=True)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
-def test_config3_shape_in_mx_formats(fmt):
-    case = synth.config_case(3, fmt)
-    ref = synth.config_case(3)
+def test_paged_decode_shape_in_mx_formats(fmt):
+    case = synth.workload_case(3, fmt)
+    ref = synth.workload_case(3)
     assert case.fmt == fmt and case.name.endswith("_" + fmt)
     assert case.kv_scale_pool is None and case.kv_sf_pool is not None
-    # the same sequences and block table as config 3
+    # the same sequences and block table as the paged decode workload
     assert np.array_equal(case.context_lens, ref.context_lens)
     assert np.array_equal(case.block_table, ref.block_table)
 
