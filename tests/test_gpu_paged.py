@@ -78,9 +78,10 @@ def test_paged_small_matrix(next_n, bs):
     _check(case, 37, f"small_n{next_n}_bs{bs}")
 
 
-@pytest.mark.parametrize("next_n,bs", [(5, 64), (6, 32), (9, 16)])
+@pytest.mark.parametrize("next_n,bs", [(5, 64), (6, 32), (9, 16), (16, 16)])
 def test_paged_more_than_four_query_tokens(next_n, bs):
-    # next_n > 4: each sequence's rows are walked in groups of 4
+    # next_n > 4: each sequence's rows are walked in groups of 4 (16 is the
+    # largest next_n the entry point takes)
     case = synth.paged_case(batch=4, next_n=next_n, h=64, d=128, block_size=bs,
                             num_blocks=500, ctx_lo=1, ctx_hi=1500, max_context_len=1603,
                             seed=100 + next_n, context_lens=[3, 700, 1603, 1025])
