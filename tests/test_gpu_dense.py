@@ -163,6 +163,39 @@ def _check_compressed(case, what):
     assert_close(packed.cpu().numpy(), ref, bound, what)
 
 
+@pytest.mark.parametrize("fmt,skv", [("fp8", (1 << 20) + 37), ("mxfp4", (1 << 19) + 37)])
+def test_long_key_range_sampled_entries(fmt, skv):
+    # keys past 2^19 / 2^20 with a ragged end: the full mask on the device,
+    # values on sampled columns of every row (each entry depends only on its
+    # key, so the oracle runs on the gathered keys), range ends included
+    sq = 8
+    ks = np.array([0, 0, 5, 1000, skv // 2, 77, skv - 100, 3], np.int32)
+    ke = np.array([skv, skv - 1, skv, skv // 2, skv, 78, skv, skv - 36], np.int32)
+    case = synth.dense_case(sq, skv, 64, 128, fmt, seed=4242, k_start=ks, k_end=ke)
+    log(f"[dense] long key range {fmt} Skv={skv}")
+    out = run_dense(case)
+    torch.cuda.synchronize()
+    assert_mask_on_device(out, case.k_start, case.k_end, skv)
+    s, e = oracle.row_ranges(case.k_start, case.k_end, skv)
+    rng = np.random.default_rng(7)
+    rows, cols = [], []
+    for r in range(sq):
+        ends = [s[r], s[r] + 1, e[r] - 2, e[r] - 1]
+        c = np.concatenate([rng.integers(s[r], e[r], 512), [x for x in ends if s[r] <= x < e[r]]])
+        c = np.unique(c)
+        rows.append(np.full(c.size, r))
+        cols.append(c)
+    rows, cols = np.concatenate(rows), np.concatenate(cols)
+    keys, at = np.unique(cols, return_inverse=True)
+    sub = lambda a: None if a is None else a[keys]
+    ref, bound = oracle.dense_entries(fmt, case.q, case.q_sf, sub(case.kv), sub(case.kv_sf),
+                                      sub(case.kv_scale), case.weights,
+                                      np.zeros(sq, np.int32), np.full(sq, keys.size, np.int32),
+                                      rows, at)
+    got = out[torch.from_numpy(rows).to(out.device), torch.from_numpy(cols).to(out.device)]
+    assert_close(got.cpu().numpy(), ref, bound, f"long_{fmt}")
+
+
 def test_compressed_2048x4096_full_parity():
     _check_compressed(synth.workload_case(2), "compressed")
 
