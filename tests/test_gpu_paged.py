@@ -131,6 +131,15 @@ def test_paged_negative_scales_and_keep_mode():
     assert_close(np.where(inside, got, -np.inf), ref, bound, "paged_keep")
 
 
+def test_paged_long_contexts():
+    # contexts of up to 2^17 tokens (2048 blocks of 64) through a permuted
+    # pool, one past max_context_len, one not a whole number of blocks
+    case = synth.paged_case(batch=3, next_n=2, h=64, d=128, block_size=64, num_blocks=7000,
+                            ctx_lo=0, ctx_hi=0, max_context_len=1 << 17, seed=517,
+                            context_lens=[(1 << 17) + 5, 70001, 99999])
+    _check(case, 256, "long_contexts")
+
+
 def test_paged_decode_64x4_full_parity_and_split_independence():
     case = synth.workload_case(3)
     import mqa_logits_amd as mq
