@@ -536,12 +536,13 @@ struct RowGroup {
   }
 };
 
-// One streamed KV operand: the MFMA B operand of a 16-token step, its e8m0
-// scale (MX) and its fp32 token scale (FP8).  The e8m0 byte is held as a
-// byte: widened where a step uses it, the widening waits only for that step's
-// loads.  Held widened, the ring's values would be widened at the top of the
-// walk's loop body, which waits for every slot's scale load, the last
-// refill's included.
+// One streamed KV operand: the MFMA B operand of a step, its e8m0 scale (MX)
+// and its fp32 token scale (FP8).  The e8m0 byte is held as a byte and
+// widened where its step uses it, so the widening waits only for that step's
+// loads.  Held as an int, the compiler narrows the ring's values to bytes
+// across the loop's back-edge and widens them all at the top of the loop
+// body, which then waits for every slot's scale load, the last refill's
+// included.
 struct KvOp {
   v8i b;
   uint8_t bs;
