@@ -79,6 +79,10 @@ struct RowGroup32 {
   float w[2][16 * kHG];                                      // rows l/32 and 2 + l/32; 0 past H
   v8i ql;
   int qls;
+  // LIN, until the linear-half operand is formed: w / 2 of the (row, head)
+  // of this lane's A row of tile m, and (MXFP8) that head's two block scales.
+  float wl[kMT];
+  int wsf[kMT];
 
   // Row (within the wave's 4) and head that A row l % 32 of tile m reads.
   __device__ static __forceinline__ int a_of(int lane, int m) {
@@ -88,8 +92,10 @@ struct RowGroup32 {
     return 16 * (m % kHG) + 4 * ((lane >> 3) & 3) + (lane & 3);
   }
 
-  // Issues the loads of the Q operands, their block scales and the weights;
-  // finish() then forms the linear-half operand and pins the operands.
+  // Issues the loads of the Q operands, their block scales and the weights
+  // (LIN: also the weight and block scales make_lin takes for each of this
+  // lane's A rows, so that forming q' waits for no further load); finish()
+  // then forms the linear-half operand and pins the operands.
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
                                        const uint8_t* __restrict__ q_sf,
                                        const void* __restrict__ wts, bool w_bf16, int row0, int sq,
@@ -101,12 +107,20 @@ struct RowGroup32 {
       const int head = head_of(lane, m);
       uint4 a = zero4(), b = zero4();
       qs[m] = 127;
+      wl[m] = 0.f;
+      wsf[m] = 127 | (127 << 8);
       if (head < H) {
         const int64_t hr = row * H + head;
         const uint8_t* src = q + hr * L::kRowBytes;
         a = *reinterpret_cast<const uint4*>(src + L::lo(g));
         if constexpr (L::hi(0) >= 0) b = *reinterpret_cast<const uint4*>(src + L::hi(g));
         if constexpr (FmtInfo<FMT>::kMX) qs[m] = (int)q_sf[hr * L::kBlocks + g];
+        if constexpr (LIN) {
+          wl[m] = 0.5f * (w_bf16 ? bf16_value(static_cast<const uint16_t*>(wts)[hr])
+                                 : static_cast<const float*>(wts)[hr]);
+          if constexpr (FmtInfo<FMT>::kMX && FMT != kMXFP4)
+            wsf[m] = (int)*reinterpret_cast<const uint16_t*>(q_sf + hr * L::kBlocks);
+        }
       }
       qa[m] = make_op(a, b);
     }
@@ -142,10 +156,8 @@ struct RowGroup32 {
   // The Q operands stay resident for the whole walk and are only read by the
   // MFMAs, which take A from AGPRs: pin them there (LIN: after forming the
   // linear-half operand from them).
-  __device__ __forceinline__ void finish(const uint8_t* __restrict__ q_sf,
-                                         const void* __restrict__ wts, bool w_bf16, int row0,
-                                         int sq, int lane, char* lin_lds) {
-    if constexpr (LIN) make_lin(q_sf, wts, w_bf16, row0, sq, lane, lin_lds);
+  __device__ __forceinline__ void finish(int lane, char* lin_lds) {
+    if constexpr (LIN) make_lin(lane, lin_lds);
 #pragma unroll
     for (int m = 0; m < kMT; ++m) asm volatile("" : "+a"(qa[m]));
     if constexpr (LIN) asm volatile("" : "+a"(ql));
@@ -160,9 +172,7 @@ struct RowGroup32 {
   // its operand of the linear tile, A row r = l % 32 = (query 2 ((r/8) % 2) +
   // (r/4) % 2, piece r % 4) for r < 16, zero rows above.  The LDS traffic stays
   // within the wave (in-order LDS access).
-  __device__ __forceinline__ void make_lin(const uint8_t* __restrict__ q_sf,
-                                           const void* __restrict__ wts, bool w_bf16, int row0,
-                                           int sq, int lane, char* lds) {
+  __device__ __forceinline__ void make_lin(int lane, char* lds) {
     constexpr bool kFP4 = FMT == kMXFP4;
     constexpr int kD = 64;
     const int g = lane >> 5;
@@ -175,7 +185,6 @@ struct RowGroup32 {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int a = 2 * p + ((lane >> 2) & 1);
-      const int64_t row = min(row0 + a, sq - 1);
       float acc[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) acc[k] = 0.f;
@@ -184,15 +193,14 @@ struct RowGroup32 {
         const int m = p * kHG + hg;
         const int head = 16 * hg + hl;
         if (head >= H) continue;
-        const int64_t hr = row * H + head;
-        const float wv = 0.5f * (w_bf16 ? bf16_value(static_cast<const uint16_t*>(wts)[hr])
-                                        : static_cast<const float*>(wts)[hr]);
+        const float wv = wl[m];
         float w_lo = wv, w_hi = wv;
         if constexpr (kFP4) {
           w_lo = ldexpf(wv, qs[m] - 127);             // block g's scale is this lane's operand's
         } else if constexpr (FmtInfo<FMT>::kMX) {
-          w_lo = ldexpf(wv, (int)q_sf[hr * L::kBlocks + e_lo / 32] - 127);
-          w_hi = ldexpf(wv, (int)q_sf[hr * L::kBlocks + e_hi / 32] - 127);
+          // elements [16g, 16g + 16) lie in block 0, [32 + 16g, 48 + 16g) in block 1
+          w_lo = ldexpf(wv, (wsf[m] & 0xff) - 127);
+          w_hi = ldexpf(wv, (wsf[m] >> 8) - 127);
         }
         if constexpr (kFP4) {
 #pragma unroll
@@ -470,6 +478,11 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
     lin_lds = lin_all[wave];
   }
 
+  // The Q operands and weights do not depend on the ranges: they go out while
+  // the ranges' (scalar) loads are in flight.
+  rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, row0, p.sq, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
   int s_r[kRowsPerWave], e_r[kRowsPerWave];
   int lo = 0x7fffffff, hi = 0;
 #pragma unroll
@@ -521,9 +534,9 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
     }
   };
 
-  // The walk's first operands, the first round of the scale scan below and
-  // the Q operands go out back to back, so their latencies overlap: the
-  // prologue waits for memory once.
+  // The walk's first operands and the first round of the scale scan below go
+  // out next; the linear-half operand is formed from the Q operands while
+  // they are in flight.
   KvOp ring[kKvStages];
   if (cl < ch) prefetch_span<32>(cl, ring, load_b);
 
@@ -541,7 +554,7 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  rg.load(p.q, p.q_sf, p.w, p.w_bf16 != 0, row0, p.sq, lane);
+  rg.finish(lane, lin_lds);
   __builtin_amdgcn_sched_barrier(0);
 
   bool flip = false;
@@ -560,9 +573,6 @@ __device__ __forceinline__ void dense_group32(const DenseParams& p, int row0, in
     // exact path)
     flip = cl < ch && __ballot(neg < 0) != 0;
   }
-
-  rg.finish(p.q_sf, p.w, p.w_bf16 != 0, row0, p.sq, lane, lin_lds);
-  __builtin_amdgcn_sched_barrier(0);
 
   Rsrc out_r;
   char* const out_base = static_cast<char*>(p.out);
