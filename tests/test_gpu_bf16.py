@@ -63,7 +63,7 @@ TYPES = [(True, False), (False, True), (True, True)]
 
 @pytest.mark.parametrize("w_bf16,out_bf16", TYPES)
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
-@pytest.mark.parametrize("h,d", [(64, 128), (16, 64)])
+@pytest.mark.parametrize("h,d", [(64, 128), (32, 64), (16, 64)])
 def test_dense_bf16_matrix(fmt, h, d, w_bf16, out_bf16):
     sq, skv = 37, 999                     # odd Skv: ragged last group, padded bf16 stride
     ks = np.arange(sq) * 7 - 20
@@ -117,7 +117,7 @@ def test_dense_bf16_keep_mode_and_guard_columns():
     _compare(masked, ref, bound, "bf16_keep")
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
 def test_compressed_bf16(fmt):
     import mqa_logits_amd as mq
     sq, skv = 70, 1501
