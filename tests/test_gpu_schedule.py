@@ -69,7 +69,7 @@ def _both(case, splits, **kw):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
-@pytest.mark.parametrize("h,d", [(64, 128), (16, 64)])
+@pytest.mark.parametrize("h,d", [(64, 128), (32, 64), (16, 64)])
 def test_scheduled_equals_unscheduled_and_oracle(fmt, h, d):
     sq, skv = 70, 1500
     ks, ke = _ranges("windows", sq, skv, h + d)
@@ -115,19 +115,20 @@ def test_scheduled_keep_mode_and_bf16():
     assert torch.equal(p16.view(torch.int16), s16.view(torch.int16))
 
 
-def test_scheduled_compressed_equals_unscheduled():
+@pytest.mark.parametrize("fmt,h,d", [("mxfp4", 64, 128), ("fp8", 32, 64), ("mxfp8", 32, 64)])
+def test_scheduled_compressed_equals_unscheduled(fmt, h, d):
     import mqa_logits_amd as mq
     sq, skv = 66, 2000
     ks, ke = _ranges("windows", sq, skv, 3)
-    case = synth.dense_case(sq, skv, 64, 128, "mxfp4", seed=23, k_start=ks, k_end=ke)
+    case = synth.dense_case(sq, skv, h, d, fmt, seed=23, k_start=ks, k_end=ke)
     d = dense_on_device(case)
     args = (d["fmt"], d["q"], d["q_sf"], d["kv"], d["kv_sf"], d["kv_scale"], d["weights"],
             d["k_start"], d["k_end"])
     sched = mq.mqa_logits_metadata(d["k_start"], d["k_end"], skv, 50)
-    log("[schedule] compressed")
+    log(f"[schedule] compressed {fmt} H={h} D={d}")
     plain, off = mq.mqa_logits_compressed(*args)
     scheduled, _ = mq.mqa_logits_compressed(*args, row_offsets=off, schedule=sched)
     torch.cuda.synchronize()
     assert torch.equal(plain.view(torch.int32), scheduled.view(torch.int32))
     ref, bound, _ = oracle.compressed_logits(*case.args())
-    assert_close(scheduled.cpu().numpy(), ref, bound, "sched_compressed")
+    assert_close(scheduled.cpu().numpy(), ref, bound, f"sched_compressed_{fmt}_h{h}_d{d}")
