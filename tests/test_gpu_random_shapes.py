@@ -1,0 +1,142 @@
+"""Seeded random shapes against the oracle: dense, compressed and paged calls
+with row counts, key counts, head counts, head dims, formats, logits types,
+ranges and output strides drawn per case (small sizes, so the oracle runs in
+milliseconds).  Every case checks the oracle's -inf mask and bound, that
+guard columns past the row width are never written, and that compressed
+offsets match the oracle bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_helpers import assert_close, dense_on_device, dev, log, paged_on_device
+
+pytestmark = pytest.mark.gpu
+
+BF16_UNIT = 2.0 ** -8
+GUARD = -5.5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mqa_logits_amd  # noqa: F401
+
+
+def _widen(bound, ref, out_dtype):
+    if out_dtype != torch.bfloat16:
+        return bound
+    fin = np.isfinite(ref)
+    return np.where(fin, bound + BF16_UNIT * (np.abs(np.where(fin, ref, 0.0)) + bound), bound)
+
+
+def _draw(rng):
+    fmt = ["fp8", "mxfp8", "mxfp4"][rng.integers(3)]
+    h = int(rng.choice([8, 16, 32, 64]))
+    d = int(rng.choice([64, 128]))
+    out_dtype = torch.bfloat16 if rng.random() < 0.3 else torch.float32
+    return fmt, h, d, out_dtype
+
+
+def _ranges(rng, sq, skv):
+    ks = rng.integers(-8, skv + 4, sq)
+    ke = ks + rng.integers(-3, skv + 1, sq)
+    kind = rng.integers(4)
+    if kind == 1:                                   # causal-like
+        ks[:] = 0
+        ke = skv - sq + np.arange(sq) + 1
+    elif kind == 2:                                 # full rows
+        ks[:] = 0
+        ke[:] = skv
+    return ks.astype(np.int64), ke.astype(np.int64)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_dense_and_compressed_random(seed):
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(7000 + seed)
+    fmt, h, d, out_dtype = _draw(rng)
+    sq = int(rng.integers(1, 70))
+    skv = int(rng.integers(1, 3000))
+    ks, ke = _ranges(rng, sq, skv)
+    clean = bool(rng.random() < 0.75)
+    schedule = bool(rng.random() < 0.3)
+    what = f"seed{seed} {fmt} H{h} D{d} Sq{sq} Skv{skv} {str(out_dtype)[6:]} clean={clean} sched={schedule}"
+    log(f"[random] dense {what}")
+    case = synth.dense_case(sq, skv, h, d, fmt, seed=8000 + seed, k_start=ks, k_end=ke)
+    dd = dense_on_device(case)
+    args = (dd["fmt"], dd["q"], dd["q_sf"], dd["kv"], dd["kv_sf"], dd["kv_scale"], dd["weights"],
+            dd["k_start"], dd["k_end"])
+    sched = mq.mqa_logits_metadata(dd["k_start"], dd["k_end"], skv, int(rng.integers(1, 300))) \
+        if schedule else None
+    # a row stride past the width, with guard columns that must survive
+    pad = int(rng.integers(0, 9)) * (2 if out_dtype == torch.bfloat16 else 1)
+    width = skv + pad + (skv & 1 if out_dtype == torch.bfloat16 else 0)
+    buf = torch.full((sq, width), GUARD, dtype=out_dtype, device="cuda")
+    out = buf[:, :skv]
+    mq.mqa_logits(*args, clean_logits=clean, out=out, schedule=sched, logits_dtype=out_dtype)
+    packed, off = mq.mqa_logits_compressed(*args, schedule=sched, logits_dtype=out_dtype)
+    torch.cuda.synchronize()
+    host = buf.float().cpu().numpy().astype(np.float64)
+    assert np.all(host[:, skv:] == GUARD), f"{what}: guard columns written"
+    ref, bound = oracle.dense_logits(*case.args())
+    b = _widen(bound, ref, out_dtype)
+    got = host[:, :skv]
+    if clean:
+        assert_close(got, ref, b, what)
+    else:
+        inside = np.isfinite(ref)
+        assert np.all(got[~inside] == GUARD), f"{what}: keep mode wrote outside the ranges"
+        assert_close(np.where(inside, got, -np.inf), ref, b, what)
+    cref, cbound, coff = oracle.compressed_logits(*case.args())
+    assert np.array_equal(off.cpu().numpy(), coff), f"{what}: row offsets"
+    assert_close(packed.float().cpu().numpy(), cref, _widen(cbound, cref, out_dtype),
+                 f"{what} compressed")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_paged_random(seed):
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(9000 + seed)
+    fmt, h, d, out_dtype = _draw(rng)
+    batch = int(rng.integers(1, 6))
+    next_n = int(rng.integers(1, 9))
+    bs = int(rng.choice([16, 32, 64]))
+    max_ctx = int(rng.integers(1, 900))
+    ctx = rng.integers(0, max_ctx + 80, batch)
+    nb = -(-max_ctx // bs)
+    num_blocks = batch * nb + int(rng.integers(0, 20))
+    clean = bool(rng.random() < 0.75)
+    splits = int(rng.integers(1, 400))
+    what = (f"seed{seed} {fmt} H{h} D{d} batch{batch} next_n{next_n} bs{bs} max_ctx{max_ctx} "
+            f"{str(out_dtype)[6:]} clean={clean} splits={splits}")
+    log(f"[random] paged {what}")
+    case = synth.paged_case(batch=batch, next_n=next_n, h=h, d=d, block_size=bs,
+                            num_blocks=num_blocks, ctx_lo=0, ctx_hi=0, max_context_len=max_ctx,
+                            fmt=fmt, seed=9500 + seed, context_lens=ctx)
+    pd = paged_on_device(case)
+    sched = mq.paged_mqa_logits_metadata(pd["context_lens"], next_n, bs, max_ctx, splits)
+    rows = batch * next_n
+    pad = int(rng.integers(0, 9)) * (2 if out_dtype == torch.bfloat16 else 1)
+    width = max_ctx + pad + (max_ctx & 1 if out_dtype == torch.bfloat16 else 0)
+    buf = torch.full((rows, width), GUARD, dtype=out_dtype, device="cuda")
+    out = buf[:, :max_ctx]
+    mq.paged_mqa_logits(fmt, pd["q"], pd["q_sf"], pd["kv_pool"], pd["kv_sf_pool"],
+                        pd["kv_scale_pool"], pd["weights"], pd["context_lens"], pd["block_table"],
+                        sched, next_n, max_ctx, clean_logits=clean, out=out,
+                        logits_dtype=out_dtype)
+    torch.cuda.synchronize()
+    host = buf.float().cpu().numpy().astype(np.float64)
+    assert np.all(host[:, max_ctx:] == GUARD), f"{what}: guard columns written"
+    ref, bound = oracle.paged_logits(*case.args())
+    b = _widen(bound, ref, out_dtype)
+    got = host[:, :max_ctx]
+    if clean:
+        assert_close(got, ref, b, what)
+    else:
+        inside = np.isfinite(ref)
+        assert np.all(got[~inside] == GUARD), f"{what}: keep mode wrote outside the ranges"
+        assert_close(np.where(inside, got, -np.inf), ref, b, what)
