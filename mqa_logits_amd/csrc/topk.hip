@@ -38,8 +38,9 @@ __device__ __forceinline__ uint32_t order_key(uint32_t bits) {
 
 template <int IN>
 struct TopkRow {
-  Rsrc r;
+  Rsrc r;                                 // the row's Skv elements
   int s;                                  // first column of the range (element offset)
+  int last;                               // the row's last column, relative to s
   // Key of column s + c (c relative to the range start).  The caller keeps
   // c inside the range.
   __device__ __forceinline__ uint32_t key(int c) const {
@@ -62,6 +63,12 @@ struct TopkRow {
       bits[1] = (uint32_t)w[0] & 0xffff0000u;
       bits[2] = (uint32_t)w[1] << 16;
       bits[3] = (uint32_t)w[1] & 0xffff0000u;
+      // The buffer checks each 4-byte half of the load against the row's
+      // end and reads a half that crosses it as zero: when the row's last
+      // column (odd Skv) opens a half, that column is read on its own.
+      const int lu = last - c;
+      if (lu == 0 || lu == 2)
+        bits[lu] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, 2 * (s + c + lu), 0, 0) << 16;
     } else {
       typedef int v4i __attribute__((ext_vector_type(4)));
       const v4i w = __builtin_amdgcn_raw_buffer_load_b128(r, 4 * (s + c), 0, 0);
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
   constexpr int kIB = IN == kBF16 ? 2 : 4;
   const TopkRow<IN> src{make_rsrc(static_cast<const char*>(p.logits) + row * p.stride * kIB,
                                   (uint32_t)(p.skv * kIB)),
-                        s};
+                        s, p.skv - 1 - s};
   int32_t* out = p.indices + row * p.out_stride;
 
   // ---- first level over the row: histogram of the top 11 bits -------------
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   constexpr int kIB = IN == kBF16 ? 2 : 4;
   const TopkRow<IN> src{make_rsrc(static_cast<const char*>(p.logits) + row * p.stride * kIB,
                                   (uint32_t)(p.skv * kIB)),
-                        s};
+                        s, p.skv - 1 - s};
   int32_t* out = p.indices + row * p.out_stride;
 
   uint32_t k[kTiles][4];

@@ -140,3 +140,27 @@ def test_paged_random(seed):
         inside = np.isfinite(ref)
         assert np.all(got[~inside] == GUARD), f"{what}: keep mode wrote outside the ranges"
         assert_close(np.where(inside, got, -np.inf), ref, b, what)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_topk_random(seed):
+    # row lengths across every register-kernel capacity and the streaming
+    # kernel, topk from 1 to past the row length, ties, fp32 and bf16 logits
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(9900 + seed)
+    sq = int(rng.integers(1, 40))
+    skv = int(rng.choice([int(rng.integers(1, 9000)), int(rng.integers(9000, 70000))]))
+    topk = int(rng.choice([1, int(rng.integers(1, 5000)), 2048]))
+    ties = bool(rng.random() < 0.6)
+    ranges = bool(rng.random() < 0.7)
+    bf16 = bool(rng.random() < 0.3)
+    what = f"seed{seed} Sq{sq} Skv{skv} topk{topk} ties={ties} ranges={ranges} bf16={bf16}"
+    log(f"[random] topk {what}")
+    x, ks, ke = synth.topk_logits(sq, skv, 9950 + seed, ties=ties, ranges=ranges)
+    t = dev(x)
+    if bf16:
+        bits = synth.encode_bf16(x)
+        x = synth.decode_bf16(bits).reshape(x.shape)
+        t = dev(bits.view(np.int16)).view(torch.bfloat16)
+    got = mq.mqa_logits_topk(t, topk, dev(ks), dev(ke)).cpu().numpy()
+    assert np.array_equal(got, oracle.topk_indices(x, topk, ks, ke)), what

@@ -132,3 +132,22 @@ def test_topk_after_dense_logits_is_a_valid_selection():
             lo = (ref[i, sel] + bound[i, sel]).min()
             hi = (ref[i, rest] - bound[i, rest]).max()
             assert hi <= lo, f"row {i}: unselected {hi} above selected {lo}"
+
+
+@pytest.mark.parametrize("skv", [7, 4095, 8191, 16383, 32767, 65535, 70001])
+def test_topk_bf16_last_column_of_an_odd_row(skv):
+    # bf16 rows of odd length whose last column holds the row's largest value:
+    # the register kernels read four columns per 8-byte load, and the last
+    # column shares its 4-byte half with the first column past the row
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(skv)
+    x = rng.standard_normal((3, skv)).astype(np.float32)
+    x[:, -1] = 8.0
+    x[1, -1] = -8.0                         # and once the smallest
+    bits = synth.encode_bf16(x)
+    xb = synth.decode_bf16(bits).reshape(x.shape)
+    t = dev(bits.view(np.int16)).view(torch.bfloat16)
+    log(f"[topk] bf16 odd row Skv={skv}")
+    for k in (1, min(skv, 5)):
+        got = mq.mqa_logits_topk(t, k).cpu().numpy()
+        assert np.array_equal(got, oracle.topk_indices(xb, k)), f"k={k}"
