@@ -1,9 +1,11 @@
 """Seeded random shapes against the oracle: dense, compressed and paged calls
 with row counts, key counts, head counts, head dims, formats, logits types,
-ranges and output strides drawn per case (small sizes, so the oracle runs in
+precisions, ranges and output strides drawn per case (small sizes, so the oracle runs in
 milliseconds).  Every case checks the oracle's -inf mask and bound, that
 guard columns past the row width are never written, and that compressed
 offsets match the oracle bit for bit."""
+
+import os
 
 import numpy as np
 import pytest
@@ -17,6 +19,8 @@ pytestmark = pytest.mark.gpu
 
 BF16_UNIT = 2.0 ** -8
 GUARD = -5.5
+# more seeds for a longer sweep: MQA_RANDOM_CASES=k multiplies the counts
+SCALE = int(os.environ.get("MQA_RANDOM_CASES", "1"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,7 +42,8 @@ def _draw(rng):
     h = int(rng.choice([8, 16, 32, 64]))
     d = int(rng.choice([64, 128]))
     out_dtype = torch.bfloat16 if rng.random() < 0.3 else torch.float32
-    return fmt, h, d, out_dtype
+    precision = "exact" if rng.random() < 0.25 else "default"
+    return fmt, h, d, out_dtype, precision
 
 
 def _ranges(rng, sq, skv):
@@ -54,17 +59,18 @@ def _ranges(rng, sq, skv):
     return ks.astype(np.int64), ke.astype(np.int64)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(40 * SCALE))
 def test_dense_and_compressed_random(seed):
     import mqa_logits_amd as mq
     rng = np.random.default_rng(7000 + seed)
-    fmt, h, d, out_dtype = _draw(rng)
+    fmt, h, d, out_dtype, precision = _draw(rng)
     sq = int(rng.integers(1, 70))
     skv = int(rng.integers(1, 3000))
     ks, ke = _ranges(rng, sq, skv)
     clean = bool(rng.random() < 0.75)
     schedule = bool(rng.random() < 0.3)
-    what = f"seed{seed} {fmt} H{h} D{d} Sq{sq} Skv{skv} {str(out_dtype)[6:]} clean={clean} sched={schedule}"
+    what = (f"seed{seed} {fmt} H{h} D{d} Sq{sq} Skv{skv} {str(out_dtype)[6:]} {precision} "
+            f"clean={clean} sched={schedule}")
     log(f"[random] dense {what}")
     case = synth.dense_case(sq, skv, h, d, fmt, seed=8000 + seed, k_start=ks, k_end=ke)
     dd = dense_on_device(case)
@@ -77,8 +83,10 @@ def test_dense_and_compressed_random(seed):
     width = skv + pad + (skv & 1 if out_dtype == torch.bfloat16 else 0)
     buf = torch.full((sq, width), GUARD, dtype=out_dtype, device="cuda")
     out = buf[:, :skv]
-    mq.mqa_logits(*args, clean_logits=clean, out=out, schedule=sched, logits_dtype=out_dtype)
-    packed, off = mq.mqa_logits_compressed(*args, schedule=sched, logits_dtype=out_dtype)
+    mq.mqa_logits(*args, clean_logits=clean, out=out, schedule=sched, logits_dtype=out_dtype,
+                  precision=precision)
+    packed, off = mq.mqa_logits_compressed(*args, schedule=sched, logits_dtype=out_dtype,
+                                           precision=precision)
     torch.cuda.synchronize()
     host = buf.float().cpu().numpy().astype(np.float64)
     assert np.all(host[:, skv:] == GUARD), f"{what}: guard columns written"
@@ -97,11 +105,11 @@ def test_dense_and_compressed_random(seed):
                  f"{what} compressed")
 
 
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", range(20 * SCALE))
 def test_paged_random(seed):
     import mqa_logits_amd as mq
     rng = np.random.default_rng(9000 + seed)
-    fmt, h, d, out_dtype = _draw(rng)
+    fmt, h, d, out_dtype, precision = _draw(rng)
     batch = int(rng.integers(1, 6))
     next_n = int(rng.integers(1, 9))
     bs = int(rng.choice([16, 32, 64]))
@@ -112,7 +120,7 @@ def test_paged_random(seed):
     clean = bool(rng.random() < 0.75)
     splits = int(rng.integers(1, 400))
     what = (f"seed{seed} {fmt} H{h} D{d} batch{batch} next_n{next_n} bs{bs} max_ctx{max_ctx} "
-            f"{str(out_dtype)[6:]} clean={clean} splits={splits}")
+            f"{str(out_dtype)[6:]} {precision} clean={clean} splits={splits}")
     log(f"[random] paged {what}")
     case = synth.paged_case(batch=batch, next_n=next_n, h=h, d=d, block_size=bs,
                             num_blocks=num_blocks, ctx_lo=0, ctx_hi=0, max_context_len=max_ctx,
@@ -127,7 +135,7 @@ def test_paged_random(seed):
     mq.paged_mqa_logits(fmt, pd["q"], pd["q_sf"], pd["kv_pool"], pd["kv_sf_pool"],
                         pd["kv_scale_pool"], pd["weights"], pd["context_lens"], pd["block_table"],
                         sched, next_n, max_ctx, clean_logits=clean, out=out,
-                        logits_dtype=out_dtype)
+                        logits_dtype=out_dtype, precision=precision)
     torch.cuda.synchronize()
     host = buf.float().cpu().numpy().astype(np.float64)
     assert np.all(host[:, max_ctx:] == GUARD), f"{what}: guard columns written"
@@ -142,7 +150,7 @@ def test_paged_random(seed):
         assert_close(np.where(inside, got, -np.inf), ref, b, what)
 
 
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", range(20 * SCALE))
 def test_topk_random(seed):
     # row lengths across every register-kernel capacity and the streaming
     # kernel, topk from 1 to past the row length, ties, fp32 and bf16 logits
