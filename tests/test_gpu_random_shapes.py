@@ -19,8 +19,10 @@ pytestmark = pytest.mark.gpu
 
 BF16_UNIT = 2.0 ** -8
 GUARD = -5.5
-# more seeds for a longer sweep: MQA_RANDOM_CASES=k multiplies the counts
+# more seeds for a longer sweep: MQA_RANDOM_CASES=k multiplies the counts;
+# MQA_RANDOM_SIZE=f multiplies the key counts and context lengths drawn
 SCALE = int(os.environ.get("MQA_RANDOM_CASES", "1"))
+SIZE = int(os.environ.get("MQA_RANDOM_SIZE", "1"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -65,7 +67,7 @@ def test_dense_and_compressed_random(seed):
     rng = np.random.default_rng(7000 + seed)
     fmt, h, d, out_dtype, precision = _draw(rng)
     sq = int(rng.integers(1, 70))
-    skv = int(rng.integers(1, 3000))
+    skv = int(rng.integers(1, 3000 * SIZE))
     ks, ke = _ranges(rng, sq, skv)
     clean = bool(rng.random() < 0.75)
     schedule = bool(rng.random() < 0.3)
@@ -111,9 +113,9 @@ def test_paged_random(seed):
     rng = np.random.default_rng(9000 + seed)
     fmt, h, d, out_dtype, precision = _draw(rng)
     batch = int(rng.integers(1, 6))
-    next_n = int(rng.integers(1, 9))
+    next_n = int(rng.integers(1, 9 if SIZE == 1 else 17))
     bs = int(rng.choice([16, 32, 64]))
-    max_ctx = int(rng.integers(1, 900))
+    max_ctx = int(rng.integers(1, 900 * SIZE))
     ctx = rng.integers(0, max_ctx + 80, batch)
     nb = -(-max_ctx // bs)
     num_blocks = batch * nb + int(rng.integers(0, 20))
