@@ -1,6 +1,7 @@
 """Seeded random shapes against the oracle: dense, compressed and paged calls
 with row counts, key counts, head counts, head dims, formats, logits types,
-precisions, ranges and output strides drawn per case (small sizes, so the oracle runs in
+precisions, ranges, output strides and (FP8) negative or zero token scales
+drawn per case (small sizes, so the oracle runs in
 milliseconds).  Every case checks the oracle's -inf mask and bound, that
 guard columns past the row width are never written, and that compressed
 offsets match the oracle bit for bit."""
@@ -75,6 +76,10 @@ def test_dense_and_compressed_random(seed):
             f"clean={clean} sched={schedule}")
     log(f"[random] dense {what}")
     case = synth.dense_case(sq, skv, h, d, fmt, seed=8000 + seed, k_start=ks, k_end=ke)
+    if fmt == "fp8" and rng.random() < 0.5:         # negative and zero token scales
+        flip = rng.random(skv) < 0.3
+        case.kv_scale[flip] *= -1.0
+        case.kv_scale[rng.random(skv) < 0.05] = 0.0
     dd = dense_on_device(case)
     args = (dd["fmt"], dd["q"], dd["q_sf"], dd["kv"], dd["kv_sf"], dd["kv_scale"], dd["weights"],
             dd["k_start"], dd["k_end"])
@@ -127,6 +132,11 @@ def test_paged_random(seed):
     case = synth.paged_case(batch=batch, next_n=next_n, h=h, d=d, block_size=bs,
                             num_blocks=num_blocks, ctx_lo=0, ctx_hi=0, max_context_len=max_ctx,
                             fmt=fmt, seed=9500 + seed, context_lens=ctx)
+    if fmt == "fp8" and rng.random() < 0.5:         # negative and zero token scales
+        pool = case.kv_scale_pool
+        sign = np.where(rng.random(pool.shape) < 0.3, -1.0, 1.0).astype(np.float32)
+        case.kv_scale_pool = pool * sign
+        case.kv_scale_pool[rng.random(pool.shape) < 0.05] = 0.0
     pd = paged_on_device(case)
     sched = mq.paged_mqa_logits_metadata(pd["context_lens"], next_n, bs, max_ctx, splits)
     rows = batch * next_n
