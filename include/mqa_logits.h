@@ -88,10 +88,13 @@ typedef enum {
  *   (block scales included); group sums add in fp32.  A dot's error is then
  *   below sum over groups of 7 * 2^(E - 13) <= 2^-10.2 * sum_d |q_d kv_d|: it
  *   is bounded by the products, not by the dot, so cancelling dots can lose
- *   all their low bits.  With H = 64 the linear half of ReLU comes from the
- *   weighted query sum rounded to four e4m3 pieces (about 2^-16 of each
- *   32-element block's largest magnitude).  H <= 16 and MXFP4 elements are
- *   exact per product in this mode too (as below).
+ *   all their low bits.  With H = 64, and with H = 32 when D = 64, the
+ *   linear half of ReLU comes from the weighted query sum rounded to four
+ *   e4m3 pieces (about 2^-16 of each 32-element block's largest magnitude),
+ *   in every format.  Products are exact in this mode too for H <= 16 and
+ *   for MXFP4 elements (as below).  Block scales spread over many octaves
+ *   reach the same error class as cancelling dots: a dot is then dominated
+ *   by its largest-scaled blocks.
  * MQA_PRECISION_EXACT_PRODUCTS: every product reaches the fp32 accumulation
  *   exactly (the KV operand is issued once per element of each group of 8),
  *   and ReLU is evaluated per head.  For FP8 and MXFP8 with H = 32 or 64 this

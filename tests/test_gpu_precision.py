@@ -27,6 +27,20 @@ from tests.gpu_helpers import (assert_close, dense_class_bound, default_class_bo
 pytestmark = pytest.mark.gpu
 
 CASES = [(fmt, h, d) for fmt in ("fp8", "mxfp8") for h in (32, 64) for d in (64, 128)]
+WIDE = [(fmt, h, d) for fmt in ("mxfp8", "mxfp4") for h in (32, 64) for d in (64, 128)]
+
+
+def uses_linear_half(h, d):
+    """The dense kernels' default precision takes ReLU's linear half on the
+    matrix core for H = 64, and for H = 32 with D = 64 (32x32x64 tiles)."""
+    return h == 64 or (h == 32 and d == 64)
+
+
+def _spread_block_scales(rng, sf, octaves=30):
+    """Move every e8m0 block scale by up to +-octaves (NaN codes kept)."""
+    keep = sf == 0xFF
+    moved = np.clip(sf.astype(np.int64) + rng.integers(-octaves, octaves + 1, sf.shape), 90, 164)
+    sf[...] = np.where(keep, sf, moved).astype(np.uint8)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -71,7 +85,7 @@ def test_default_precision_stays_in_its_error_class_on_cancelling_dots(fmt, h, d
     log(f"[precision] default dense {fmt} H={h} D={d}")
     got = _dense(case, "default")
     ref, bound = oracle.dense_logits(*case.args())
-    extra = dense_class_bound(case, lin=(h == 64))
+    extra = dense_class_bound(case, lin=uses_linear_half(h, d))
     assert_close(got, ref, bound + np.where(np.isfinite(ref), extra, 0.0),
                  f"default_class_cancel_{fmt}_h{h}_d{d}")
     inside = np.isfinite(ref)
@@ -160,3 +174,41 @@ def test_exact_products_on_random_inputs(fmt, h, d):
     got = _dense(case, "exact")
     ref, bound = oracle.dense_logits(*case.args())
     assert_close(got, ref, bound, f"exact_random_{fmt}_h{h}_d{d}")
+
+
+# Block scales spread over +-30 octaves: a dot is then dominated by its
+# largest-scaled blocks and the rest of it sits far below their size, which the
+# matrix core's grouped summation (and the linear half's pieces) resolve only
+# to the default precision's error class, like the cancelling dots above.
+
+@pytest.mark.parametrize("fmt,h,d", WIDE)
+def test_wide_mx_block_scales_both_precisions(fmt, h, d):
+    sq, skv = 33, 700
+    ks = np.arange(sq) * 5
+    ke = skv - 30 + np.arange(sq)
+    case = synth.dense_case(sq, skv, h, d, fmt, seed=5100 + h + d, k_start=ks, k_end=ke)
+    rng = np.random.default_rng(77 + h + d)
+    _spread_block_scales(rng, case.q_sf)
+    _spread_block_scales(rng, case.kv_sf)
+    ref, bound = oracle.dense_logits(*case.args())
+    log(f"[precision] wide block scales {fmt} H={h} D={d}")
+    assert_close(_dense(case, "exact"), ref, bound, f"exact_wide_{fmt}_h{h}_d{d}")
+    got = _dense(case, "default")
+    extra = dense_class_bound(case, lin=uses_linear_half(h, d))
+    assert_close(got, ref, bound + np.where(np.isfinite(ref), extra, 0.0),
+                 f"default_class_wide_{fmt}_h{h}_d{d}")
+    inside = np.isfinite(ref)
+    lit = float((np.abs(got[inside] - ref[inside]) / bound[inside]).max())
+    log(f"   literal-bound ratio of the default precision: {lit:.3g}")
+
+
+@pytest.mark.parametrize("fmt,h,d", [("mxfp8", 64, 128), ("mxfp4", 32, 64)])
+def test_paged_wide_mx_block_scales_exact_products(fmt, h, d):
+    case = synth.paged_case(batch=4, next_n=3, h=h, d=d, block_size=32, num_blocks=200,
+                            ctx_lo=50, ctx_hi=900, max_context_len=1000, fmt=fmt, seed=5200 + h)
+    rng = np.random.default_rng(88 + h)
+    _spread_block_scales(rng, case.q_sf)
+    _spread_block_scales(rng, case.kv_sf_pool)
+    ref, bound = oracle.paged_logits(*case.args())
+    log(f"[precision] paged wide block scales {fmt} H={h} D={d}")
+    assert_close(_paged(case, "exact"), ref, bound, f"paged_exact_wide_{fmt}_h{h}_d{d}")
