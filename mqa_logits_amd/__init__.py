@@ -98,6 +98,13 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _rows_ptr(t, what):
+    """A 2-D tensor whose rows are contiguous (its row stride is passed apart)."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{what} rows must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -262,7 +269,8 @@ def paged_mqa_logits(fmt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
         raise ValueError("logits rows must be contiguous")
     _check(lib.paged_mqa_logits(
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv_pool), _ptr(kv_sf_pool), _ptr(kv_scale_pool),
-        _ptr(weights), _ptr(context_lens), _ptr(block_table), block_table.stride(0),
+        _ptr(weights), _ptr(context_lens), _rows_ptr(block_table, "block_table"),
+        block_table.stride(0),
         _ptr(schedule), ctypes.c_void_p(out.data_ptr()), out.stride(0), batch, next_n, h,
         _head_dim(fmt, q), block_size, num_blocks, max_context_len, num_splits,
         1 if clean_logits else 0, _float_type(weights.dtype, "weights"),

@@ -192,3 +192,16 @@ def test_missing_device_is_reported_as_hip_error():
     assert "device" in lib.mqa_last_error().decode().lower()
     with pytest.raises(mq.MqaError):
         mq.mqa_num_cus(0)
+
+
+def test_binding_passes_row_strided_tables_and_rejects_others():
+    # the block table and the logits rows may sit inside wider buffers (their
+    # row stride goes to the library); a table whose rows are not contiguous
+    # is refused before any call
+    import mqa_logits_amd as mq
+    wide = torch.zeros(3, 10, dtype=torch.int32)
+    assert mq._rows_ptr(wide[:, :7], "block_table").value == wide.data_ptr()
+    with pytest.raises(ValueError, match="rows must be contiguous"):
+        mq._rows_ptr(wide.t(), "block_table")
+    with pytest.raises(ValueError, match="rows must be contiguous"):
+        mq._rows_ptr(wide[:, ::2], "block_table")

@@ -1,7 +1,7 @@
 """Seeded random shapes against the oracle: dense, compressed and paged calls
 with row counts, key counts, head counts, head dims, formats, logits types,
-precisions, ranges, output strides and (FP8) negative or zero token scales
-drawn per case (small sizes, so the oracle runs in
+precisions, ranges, output, block-table and logits row strides and (FP8)
+negative or zero token scales drawn per case (small sizes, so the oracle runs in
 milliseconds).  Every case checks the oracle's -inf mask and bound, that
 guard columns past the row width are never written, and that compressed
 offsets match the oracle bit for bit."""
@@ -138,6 +138,11 @@ def test_paged_random(seed):
         case.kv_scale_pool = pool * sign
         case.kv_scale_pool[rng.random(pool.shape) < 0.05] = 0.0
     pd = paged_on_device(case)
+    if rng.random() < 0.5:                          # a block table with a wider row stride
+        wide = torch.full((batch, case.block_table.shape[1] + int(rng.integers(1, 7))), -1,
+                          dtype=torch.int32, device="cuda")
+        wide[:, :case.block_table.shape[1]] = pd["block_table"]
+        pd["block_table"] = wide[:, :case.block_table.shape[1]]
     sched = mq.paged_mqa_logits_metadata(pd["context_lens"], next_n, bs, max_ctx, splits)
     rows = batch * next_n
     pad = int(rng.integers(0, 9)) * (2 if out_dtype == torch.bfloat16 else 1)
@@ -182,5 +187,10 @@ def test_topk_random(seed):
         bits = synth.encode_bf16(x)
         x = synth.decode_bf16(bits).reshape(x.shape)
         t = dev(bits.view(np.int16)).view(torch.bfloat16)
+    if rng.random() < 0.5:                          # rows inside a wider buffer
+        wide = torch.full((sq, skv + int(rng.integers(1, 9))), float("nan"), dtype=t.dtype,
+                          device="cuda")
+        wide[:, :skv] = t
+        t = wide[:, :skv]
     got = mq.mqa_logits_topk(t, topk, dev(ks), dev(ke)).cpu().numpy()
     assert np.array_equal(got, oracle.topk_indices(x, topk, ks, ke)), what
