@@ -242,6 +242,9 @@ mqa_status paged_mqa_logits_metadata(const int32_t* context_lens, int32_t batch,
  *   context_lens [batch] int32: tokens of sequence b including its next_n new
  *            ones; logical token j of b is slot j % block_size of physical
  *            block block_table[b * block_table_stride + j / block_size]
+ *            (row b is read up to entry ceil(min(ctx_b, max_context_len) /
+ *            block_size); ids are clamped to [0, num_blocks); the Python
+ *            binding requires rows of ceil(max_context_len / block_size))
  *   schedule from paged_mqa_logits_metadata with the same arguments
  *   logits   [batch*next_n, logits_stride] of logits_type, logits_stride >=
  *            max_context_len (even for bf16; the pointer 4-byte aligned).

@@ -98,6 +98,64 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+I32_T, I64_T = (torch.int32,), (torch.int64,)
+
+
+class _Args:
+    """The tensor arguments of one call, checked against what the C ABI will
+    read or write through their pointers: shape (None entries are free),
+    element type or size, layout (contiguous, or rows contiguous when
+    `rows`), then one GPU for all of them.  The library sees only pointers
+    and sizes, so a mismatch would read or write outside a tensor."""
+
+    def __init__(self):
+        self.seen = []
+
+    def want(self, t, name, shape, dtypes=None, itemsize=None, rows=False):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
+        if itemsize is not None and t.element_size() != itemsize:
+            raise ValueError(f"{name} must have {itemsize}-byte elements, got {t.dtype}")
+        if rows:
+            if t.stride(-1) != 1:
+                raise ValueError(f"{name} rows must be contiguous")
+        elif not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.seen.append((name, t))
+
+    def on_gpu(self):
+        first = self.seen[0][1].device
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a GPU tensor (the library reads device memory)")
+            if t.device != first:
+                raise ValueError(f"{name} must be on {first}, got {t.device}")
+
+
+def _codes(a, fmt, q, kv, q_sf, kv_sf, kv_scale, rows_shape, kv_shape):
+    """The Q and KV operands of a call: byte codes (two e2m1 per byte for
+    mxfp4), e8m0 block scales for the MX formats, fp32 token scales for fp8.
+    rows_shape: Q's leading dims; kv_shape: KV's leading dims.  Returns D."""
+    _fmt(fmt)
+    d = _head_dim(fmt, q)
+    a.want(q, "q", (*rows_shape, q.shape[-1] if q.dim() else None), itemsize=1)
+    a.want(kv, "kv", (*kv_shape, q.shape[-1]), itemsize=1)
+    if fmt == "fp8":
+        if q_sf is not None or kv_sf is not None:
+            raise ValueError("fp8 takes no block scales (q_sf, kv_sf)")
+        a.want(kv_scale, "kv_scale", tuple(kv_shape), (torch.float32,))
+    else:
+        if kv_scale is not None:
+            raise ValueError(f"{fmt} takes no kv_scale")
+        a.want(q_sf, "q_sf", (*rows_shape, d // 32), itemsize=1)
+        a.want(kv_sf, "kv_sf", (*kv_shape, d // 32), itemsize=1)
+    return d
+
+
 def _rows_ptr(t, what):
     """A 2-D tensor whose rows are contiguous (its row stride is passed apart)."""
     if t.dim() != 2 or t.stride(1) != 1:
@@ -158,13 +216,29 @@ def _schedule(schedule):
     return _ptr(schedule), schedule.shape[0] - 1
 
 
+def _dense_args(a, fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, schedule):
+    sq, h = weights.shape
+    _codes(a, fmt, q, kv, q_sf, kv_sf, kv_scale, (sq, h), (kv.shape[0],))
+    a.want(weights, "weights", (sq, h), tuple(FLOAT_TYPES))
+    a.want(k_start, "k_start", (sq,), I32_T)
+    a.want(k_end, "k_end", (sq,), I32_T)
+    if schedule is not None:
+        a.want(schedule, "schedule", (None, 2), I32_T)
+
+
 def mqa_logits_metadata(k_start, k_end, skv, num_splits=None, out=None):
     """int32 [num_splits + 1, 2] work schedule for mqa_logits /
     mqa_logits_compressed with these ranges."""
+    a = _Args()
     if num_splits is None:
         num_splits = paged_mqa_logits_default_splits(k_start.device.index or 0)
+    sq = k_start.shape[0]
+    a.want(k_start, "k_start", (sq,), I32_T)
+    a.want(k_end, "k_end", (sq,), I32_T)
     if out is None:
         out = torch.empty(num_splits + 1, 2, dtype=torch.int32, device=k_start.device)
+    a.want(out, "out", (num_splits + 1, 2), I32_T)
+    a.on_gpu()
     _check(lib.mqa_logits_metadata(_ptr(k_start), _ptr(k_end), k_start.shape[0], skv,
                                    num_splits, _ptr(out), _stream(k_start)))
     return out
@@ -179,10 +253,12 @@ def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
     "default" or "exact" (mqa_precision)."""
     sq, h = weights.shape
     skv = kv.shape[0]
+    a = _Args()
+    _dense_args(a, fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, schedule)
     if out is None:
         out = _logits_rows(sq, skv, logits_dtype, q.device)
-    if out.stride(1) != 1:
-        raise ValueError("logits rows must be contiguous")
+    a.want(out, "out", (sq, skv), tuple(FLOAT_TYPES), rows=True)
+    a.on_gpu()
     _check(lib.mqa_logits(
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv), _ptr(kv_sf), _ptr(kv_scale),
         _ptr(weights), _ptr(k_start), _ptr(k_end), ctypes.c_void_p(out.data_ptr()),
@@ -196,11 +272,18 @@ def mqa_logits(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end,
 def mqa_logits_topk(logits, topk, k_start=None, k_end=None, out=None):
     """int32 [Sq, topk] columns of each row's topk largest non--inf logits in
     [k_start, k_end) (the whole row without ranges), ascending, -1 padded."""
+    a = _Args()
     sq, skv = logits.shape
-    if logits.stride(1) != 1:
-        raise ValueError("logits rows must be contiguous")
+    a.want(logits, "logits", (sq, skv), tuple(FLOAT_TYPES), rows=True)
+    if (k_start is None) != (k_end is None):
+        raise ValueError("k_start and k_end go together")
+    if k_start is not None:
+        a.want(k_start, "k_start", (sq,), I32_T)
+        a.want(k_end, "k_end", (sq,), I32_T)
     if out is None:
         out = torch.empty(sq, topk, dtype=torch.int32, device=logits.device)
+    a.want(out, "out", (sq, topk), I32_T, rows=True)
+    a.on_gpu()
     _check(lib.mqa_logits_topk(
         ctypes.c_void_p(logits.data_ptr()), _float_type(logits.dtype, "logits"),
         logits.stride(0) if sq > 0 else skv, _ptr(k_start), _ptr(k_end), sq, skv, topk,
@@ -211,9 +294,14 @@ def mqa_logits_topk(logits, topk, k_start=None, k_end=None, out=None):
 
 def mqa_logits_compressed_offsets(k_start, k_end, skv, out=None):
     """int64 [Sq + 1] exclusive prefix sum of the clamped row lengths."""
+    a = _Args()
     sq = k_start.shape[0]
+    a.want(k_start, "k_start", (sq,), I32_T)
+    a.want(k_end, "k_end", (sq,), I32_T)
     if out is None:
         out = torch.empty(sq + 1, dtype=torch.int64, device=k_start.device)
+    a.want(out, "out", (sq + 1,), I64_T)
+    a.on_gpu()
     _check(lib.mqa_logits_compressed_offsets(_ptr(k_start), _ptr(k_end), sq, skv,
                                              _ptr(out), _stream(k_start)))
     return out
@@ -228,10 +316,17 @@ def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k
     Without `out`, the total length is read back from the device (a sync)."""
     sq, h = weights.shape
     skv = kv.shape[0]
+    a = _Args()
+    _dense_args(a, fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k_end, schedule)
     if row_offsets is None:
         row_offsets = mqa_logits_compressed_offsets(k_start, k_end, skv)
+    a.want(row_offsets, "row_offsets", (sq + 1,), I64_T)
     if out is None:
         out = torch.empty(int(row_offsets[-1].item()), dtype=logits_dtype, device=q.device)
+    # out must hold row_offsets[-1] values (not checked here: that would read
+    # the offsets back from the device)
+    a.want(out, "out", (None,), tuple(FLOAT_TYPES))
+    a.on_gpu()
     _check(lib.mqa_logits_compressed(
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv), _ptr(kv_sf), _ptr(kv_scale),
         _ptr(weights), _ptr(k_start), _ptr(k_end), _ptr(row_offsets), _ptr(out),
@@ -244,10 +339,14 @@ def mqa_logits_compressed(fmt, q, q_sf, kv, kv_sf, kv_scale, weights, k_start, k
 def paged_mqa_logits_metadata(context_lens, next_n, block_size, max_context_len,
                               num_splits=None, out=None):
     """int32 [num_splits + 1, 2] schedule for paged_mqa_logits."""
+    a = _Args()
     if num_splits is None:
         num_splits = paged_mqa_logits_default_splits(context_lens.device.index or 0)
+    a.want(context_lens, "context_lens", (context_lens.shape[0],), I32_T)
     if out is None:
         out = torch.empty(num_splits + 1, 2, dtype=torch.int32, device=context_lens.device)
+    a.want(out, "out", (num_splits + 1, 2), I32_T)
+    a.on_gpu()
     _check(lib.paged_mqa_logits_metadata(_ptr(context_lens), context_lens.shape[0], next_n,
                                          block_size, max_context_len, num_splits, _ptr(out),
                                          _stream(context_lens)))
@@ -259,14 +358,26 @@ def paged_mqa_logits(fmt, q, q_sf, kv_pool, kv_sf_pool, kv_scale_pool, weights,
                      clean_logits=True, out=None, logits_dtype=torch.float32,
                      precision="default"):
     """Paged decode logits [batch * next_n, max_context_len] of logits_dtype."""
+    a = _Args()
     batch = context_lens.shape[0]
     rows, h = weights.shape
     num_blocks, block_size = kv_pool.shape[0], kv_pool.shape[1]
     num_splits = schedule.shape[0] - 1
+    if rows != batch * next_n:
+        raise ValueError(f"weights must have batch * next_n = {batch * next_n} rows, got {rows}")
+    _codes(a, fmt, q, kv_pool, q_sf, kv_sf_pool, kv_scale_pool, (rows, h), (num_blocks, block_size))
+    a.want(weights, "weights", (rows, h), tuple(FLOAT_TYPES))
+    a.want(context_lens, "context_lens", (batch,), I32_T)
+    a.want(block_table, "block_table", (batch, None), I32_T, rows=True)
+    need = -(-max_context_len // block_size) if block_size > 0 else 0
+    if block_table.shape[1] < need:
+        raise ValueError(f"block_table rows must hold ceil(max_context_len / block_size) = {need} "
+                         f"blocks, got {block_table.shape[1]}")
+    a.want(schedule, "schedule", (num_splits + 1, 2), I32_T)
     if out is None:
         out = _logits_rows(rows, max_context_len, logits_dtype, q.device)
-    if out.stride(1) != 1:
-        raise ValueError("logits rows must be contiguous")
+    a.want(out, "out", (rows, max_context_len), tuple(FLOAT_TYPES), rows=True)
+    a.on_gpu()
     _check(lib.paged_mqa_logits(
         _fmt(fmt), _ptr(q), _ptr(q_sf), _ptr(kv_pool), _ptr(kv_sf_pool), _ptr(kv_scale_pool),
         _ptr(weights), _ptr(context_lens), _rows_ptr(block_table, "block_table"),

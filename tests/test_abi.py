@@ -205,3 +205,87 @@ def test_binding_passes_row_strided_tables_and_rejects_others():
         mq._rows_ptr(wide.t(), "block_table")
     with pytest.raises(ValueError, match="rows must be contiguous"):
         mq._rows_ptr(wide[:, ::2], "block_table")
+
+
+def _dense_inputs(fmt="fp8", sq=5, skv=40, h=16, d=64):
+    dq = d // 2 if fmt == "mxfp4" else d
+    t = dict(q=torch.zeros(sq, h, dq, dtype=torch.uint8), kv=torch.zeros(skv, dq, dtype=torch.uint8),
+             q_sf=None, kv_sf=None, kv_scale=torch.ones(skv), weights=torch.zeros(sq, h),
+             k_start=torch.zeros(sq, dtype=torch.int32), k_end=torch.full((sq,), skv, dtype=torch.int32))
+    if fmt != "fp8":
+        t.update(q_sf=torch.zeros(sq, h, d // 32, dtype=torch.uint8),
+                 kv_sf=torch.zeros(skv, d // 32, dtype=torch.uint8), kv_scale=None)
+    return t
+
+
+def _call_dense(t, fmt="fp8"):
+    import mqa_logits_amd as mq
+    return mq.mqa_logits(fmt, t["q"], t["q_sf"], t["kv"], t["kv_sf"], t["kv_scale"], t["weights"],
+                         t["k_start"], t["k_end"])
+
+
+@pytest.mark.parametrize("change,message", [
+    (dict(k_start=torch.zeros(5, dtype=torch.int64)), "k_start must be torch.int32"),
+    (dict(k_end=torch.zeros(4, dtype=torch.int32)), "k_end must have shape"),
+    (dict(kv=torch.zeros(40, 32, dtype=torch.uint8)), "kv must have shape"),
+    (dict(kv=torch.zeros(40, 64, dtype=torch.float32)), "kv must have 1-byte elements"),
+    (dict(kv_scale=torch.ones(41)), "kv_scale must have shape"),
+    (dict(kv_scale=torch.ones(40, dtype=torch.float64)), "kv_scale must be torch.float32"),
+    (dict(weights=torch.zeros(5, 16, dtype=torch.float64)), "weights must be"),
+    (dict(q=torch.zeros(5, 16, 128, dtype=torch.uint8)[:, :, ::2]), "q must be contiguous"),
+    (dict(q_sf=torch.zeros(5, 16, 2, dtype=torch.uint8)), "fp8 takes no block scales"),
+    (dict(), "q must be a GPU tensor"),
+])
+def test_binding_checks_dense_arguments_before_calling(change, message):
+    t = _dense_inputs()
+    t.update(change)
+    with pytest.raises(ValueError, match=message):
+        _call_dense(t)
+
+
+def test_binding_checks_mx_scales_and_paged_tables():
+    import mqa_logits_amd as mq
+    t = _dense_inputs("mxfp4")
+    t["kv_sf"] = torch.zeros(40, 3, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="kv_sf must have shape"):
+        _call_dense(t, "mxfp4")
+    t = _dense_inputs("mxfp8")
+    t["kv_scale"] = torch.ones(40)
+    with pytest.raises(ValueError, match="takes no kv_scale"):
+        _call_dense(t, "mxfp8")
+    # paged: rows of the weights must be batch * next_n, the block table int32
+    q = torch.zeros(6, 16, 64, dtype=torch.uint8)
+    pool = torch.zeros(10, 16, 64, dtype=torch.uint8)
+    scales = torch.ones(10, 16)
+    ctx = torch.tensor([5, 9], dtype=torch.int32)
+    sched = torch.zeros(5, 2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="batch \\* next_n"):
+        mq.paged_mqa_logits("fp8", q, None, pool, None, scales, torch.zeros(5, 16), ctx,
+                            torch.zeros(2, 4, dtype=torch.int32), sched, 3, 64)
+    with pytest.raises(ValueError, match="block_table must be torch.int32"):
+        mq.paged_mqa_logits("fp8", q, None, pool, None, scales, torch.zeros(6, 16), ctx,
+                            torch.zeros(2, 4, dtype=torch.int64), sched, 3, 64)
+    with pytest.raises(ValueError, match="k_start and k_end go together"):
+        mq.mqa_logits_topk(torch.zeros(3, 10), 2, torch.zeros(3, dtype=torch.int32))
+
+
+def test_binding_requires_block_tables_wide_enough_for_max_context_len():
+    # the library reads row b of the table up to ceil(min(ctx_b, max_ctx) / bs)
+    # entries; the binding cannot see ctx_b without a device read, so it asks
+    # for rows of ceil(max_ctx / bs)
+    import mqa_logits_amd as mq
+    batch, next_n, h, d, bs, nblk, max_ctx = 2, 2, 8, 64, 16, 12, 40
+    rows = batch * next_n
+    q = torch.zeros(rows, h, d, dtype=torch.uint8)
+    kv = torch.zeros(nblk, bs, d, dtype=torch.uint8)
+    kvs = torch.ones(nblk, bs)
+    w = torch.ones(rows, h)
+    ctx = torch.full((batch,), max_ctx, dtype=torch.int32)
+    sched = torch.zeros(3, 2, dtype=torch.int32)
+    narrow = torch.zeros(batch, 2, dtype=torch.int32)           # needs 3
+    with pytest.raises(ValueError, match="block_table rows must hold .* = 3 blocks, got 2"):
+        mq.paged_mqa_logits("fp8", q, None, kv, None, kvs, w, ctx, narrow, sched, next_n, max_ctx)
+    # the width check passes at 3; the next refusal is the CPU tensor
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        mq.paged_mqa_logits("fp8", q, None, kv, None, kvs, w, ctx,
+                            torch.zeros(batch, 3, dtype=torch.int32), sched, next_n, max_ctx)
