@@ -117,7 +117,7 @@ constexpr int kTopkCap = 4 * kTopkThreads;   // LDS list capacity of the two-pas
 constexpr int kHistStride = 2048 + 16;
 
 struct TopkShared {
-  uint32_t hist[kHistStride];
+  alignas(16) uint32_t hist[kHistStride];   // 16-byte rows: read as 4-bin vectors
   uint64_t wave_sums64[kTopkWaves];
   uint32_t wave_sums32[kTopkWaves];
   uint32_t sel_bin, sel_above;
@@ -377,12 +377,94 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
   for (int pos = (int)n_sel + t; pos < p.topk; pos += kTopkThreads) out[pos] = -1;
 }
 
+// ---- wave-level helpers of the register kernel's prefilter ------------------
+// Inclusive scans over the wave with DPP moves (ALU latency, no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16, then row 0's
+// and row 1's last lanes broadcast to the rows after them.  `id` is the
+// operation's identity, which lanes without a source contribute.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x, uint32_t id, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+struct OpAdd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+struct OpMin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, 0u, OpMax{}), kWaveLanes - 1);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, ~0u, OpMin{}), kWaveLanes - 1);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, 0u, OpAdd{}), kWaveLanes - 1);
+}
+
+// One radix level over a 256-bin histogram h (bin 255 holds the largest
+// keys): the bin holding the need-th largest key, the count in higher bins
+// and the bin's own count.  Every wave reads the histogram and reaches the
+// same answer, so no second barrier is needed.  1 <= need <= the total.
+struct BinPick {
+  uint32_t bin, above, count;
+};
+__device__ __forceinline__ BinPick pick_bin256(const uint32_t* h, uint32_t need) {
+  const int lane = threadIdx.x & (kWaveLanes - 1);
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  uint32_t local;
+  {
+    const v4u v = *reinterpret_cast<const v4u*>(h + 252 - 4 * lane);   // bins 252-4l .. 255-4l
+    local = v[0] + v[1] + v[2] + v[3];
+  }
+  const uint32_t incl = wave_scan_u32(local, 0u, OpAdd{});
+  // the lane whose four bins reach need; its bins are read again (one address
+  // for the whole wave) and searched on the scalar unit
+  const uint64_t hit = __ballot(incl - local < need && incl >= need);
+  const int src = hit ? __builtin_ctzll(hit) : 0;
+  uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(incl - local), src);
+  const v4u w = *reinterpret_cast<const v4u*>(h + 252 - 4 * src);
+  uint32_t bin = 255 - 4 * src, cnt = 0;
+#pragma unroll
+  for (int j = 3; j >= 0; --j, --bin) {      // bins 255-4src down to 252-4src
+    cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)w[j]);
+    if (run + cnt >= need) break;
+    run += cnt;
+  }
+  return {bin, run, cnt};
+}
+
 // Rows of up to kTopkThreads * R columns: the row is read once, into
 // registers (thread t holds columns 4t .. 4t+3 of every 4096-column tile, so
-// the loads coalesce), and every level and the ordered write work from there.
-// After the first level the keys in its bin are gathered (in any order) into
-// LDS and the finer levels histogram that short list.  The selection is then
-// marked in LDS bitmaps over the columns, which give column order directly.
+// the loads coalesce), and the selection works from there.
+//   * Prefilter (rows longer than topk, topk up to half the list): a
+//     threshold T is taken from a sample of the row's keys (kSamples per
+//     thread, spread over the tiles), at the sample's r-th largest key with r
+//     set so that the row holds at least topk keys >= T by a margin of three
+//     standard deviations of the sampling and well under the list's capacity.
+//     A wave counts its keys >= T (and its candidates), reserves that many
+//     slots of an LDS list with one atomic and appends the keys with their
+//     columns (ballot offsets); the radix levels then run over that list
+//     only, over the bits in which T and the row's largest key differ (8 bits
+//     a level, each wave scanning the histogram itself), and the selection is
+//     marked in LDS bitmaps over the columns from the list.  A row with at
+//     most topk candidates takes them all.  If the row holds fewer than topk
+//     keys >= T, or the list overflows, the full selection below runs
+//     instead: the result is the same, only slower.
+//   * Full selection: the first level histograms every key (11 bits), the keys
+//     in its bin are gathered into LDS and the finer levels histogram that
+//     short list; the selection is marked in the bitmaps from the registers.
+//   * The bitmaps give column order directly: a block scan over 32-column
+//     words places each word's columns.
 // Up to 32 keys per thread: at most 64 VGPRs, so two blocks (8 waves per
 // SIMD) share a compute unit and one block's loads overlap the other's work.
 template <int IN, int R>
@@ -390,8 +472,11 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   static_assert(R % 4 == 0 && R <= 64, "whole 4-column groups; the flag words hold 64");
   constexpr int kTiles = R / 4;
   constexpr int kTile = 4 * kTopkThreads;
-  __shared__ TopkShared sh;
   constexpr int kWords = kTiles * kTile / 32;  // 32-column words of the register-held row
+  constexpr int kCap = R > 32 ? 8192 : 5120;   // LDS list: prefilter keys, or one bin's keys
+  constexpr int kSamples = R >= 32 ? R / 16 : 1;
+  static_assert((kTiles & (kTiles - 1)) == 0 && kTiles % kSamples == 0, "sample tiles");
+  __shared__ TopkShared sh;
   __shared__ union {
     uint32_t hist_more[3 * kHistStride];      // copies 1..3 of the first-level histogram
     uint32_t maps[2 * kWords];                // then the column bitmaps (key > K, key == K)
@@ -399,10 +484,15 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   uint32_t* const hist_more = u_.hist_more;
   uint32_t* const gmap = u_.maps;
   uint32_t* const qmap = u_.maps + kWords;
-  __shared__ uint32_t bin_keys[kTopkCap];     // the first-level bin's keys
+  __shared__ uint32_t bin_keys[kCap];         // the prefilter's keys, or the first-level bin's
+  __shared__ uint16_t list_col[kCap];         // the prefilter's columns (range-relative)
+  __shared__ uint32_t smp_stat[3][kTopkWaves];
+  __shared__ uint32_t list_stat[2][kTopkWaves];
+  __shared__ uint32_t list_count;
   __shared__ uint32_t bin_count;
   const int t = threadIdx.x;
   const int lane = t & (kWaveLanes - 1);
+  const int wave = t >> 6;
   const int64_t row = blockIdx.x;
   int s = 0, e = p.skv;
   if (p.k_start) {
@@ -420,119 +510,283 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
 #pragma unroll
   for (int m = 0; m < kTiles; ++m) src.key4(m * kTile + 4 * t, n, k[m]);
 
-  // ---- first level: every key, no branch; -inf counts into a spare slot ----
-  // Each quarter of a wave counts into its own copy of the histogram (most
-  // keys fall in a few bins), folded before the search.
-  const int copy = lane >> 4;
-  for (int b = t; b < kHistStride; b += kTopkThreads) sh.hist[b] = 0;
-  for (int b = t; b < 3 * kHistStride; b += kTopkThreads) hist_more[b] = 0;
-  if (t == 0) bin_count = 0;
-  __syncthreads();
-  {
-    uint32_t* h = copy > 0 ? hist_more + (copy - 1) * kHistStride : sh.hist;
+  // keys > K are taken, then the first need_eq keys equal to K in column order
+  uint32_t K = 0, need_eq = 0;
+  bool take_all = n <= p.topk;                // every candidate is taken
+  bool fast = false;                          // the prefilter marked the selection
+
+  if (!take_all && p.topk <= kCap / 2) {
+    for (int b = t; b < 2048; b += kTopkThreads) sh.hist[b] = 0;
+    for (int w = t; w < 2 * kWords; w += kTopkThreads) u_.maps[w] = 0;
+    if (t == 0) list_count = 0;
+    // ---- the sample: kSamples keys per thread, tiles spread over the row ----
+    uint32_t smp[kSamples];
+    uint32_t vmin = ~0u, vmax = 0, n_in = 0, n_val = 0;
+#pragma unroll
+    for (int q = 0; q < kSamples; ++q) {
+      const int tq = (t + q * (kTiles / kSamples)) & (kTiles - 1);
+      uint32_t v = k[0][0];
+#pragma unroll
+      for (int m = 1; m < kTiles; ++m) v = tq == m ? k[m][0] : v;
+      smp[q] = v;
+      const bool valid = v != kKeyNegInf;     // columns past the range hold -inf keys
+      vmin = valid ? min(vmin, v) : vmin;
+      vmax = valid ? max(vmax, v) : vmax;
+      n_in += __popcll(__ballot(tq * kTile + 4 * t < n));
+      n_val += __popcll(__ballot(valid));
+    }
+    vmin = wave_min_u32(vmin);
+    vmax = wave_max_u32(vmax);
+    if (lane == 0) {
+      smp_stat[0][wave] = vmin;
+      smp_stat[1][wave] = vmax;
+      smp_stat[2][wave] = n_in | n_val << 16;
+    }
+    __syncthreads();
+    const bool wl = lane < kTopkWaves;
+    const uint32_t mn = wave_min_u32(wl ? smp_stat[0][lane] : ~0u);
+    const uint32_t mx = wave_max_u32(wl ? smp_stat[1][lane] : 0u);
+    const uint32_t packed = wave_sum_u32(wl ? smp_stat[2][lane] : 0u);
+    const uint32_t s_in = packed & 0xffffu, s_val = packed >> 16;
+
+    // ---- the threshold: the lower edge of the sample's bin holding rank r ----
+    // A sample key stands for rho row columns; with r sample keys >= T the
+    // row's count of keys >= T is about r * rho, with a standard deviation of
+    // about rho * sqrt(r).  r solves r * rho - 3 rho sqrt(r) = topk; the
+    // refinement stops once at most r_hi sample keys are >= T.
+    uint32_t T = 0;
+    if (s_val > 0) {
+      const float rho = (float)n / (float)s_in;
+      const float x = 1.5f + sqrtf(2.25f + (float)p.topk / rho);
+      uint32_t need = min((uint32_t)ceilf(x * x), s_val);
+      const uint32_t r_hi = max(need, (uint32_t)(0.7f * (float)kCap / rho));
+      uint32_t pre = 0, got = s_val, acc = 0;
+      int pos = 32 - __clz(mx - mn);          // offset bits below the common prefix
+      for (int lvl = 0; pos > 0 && got > r_hi; ++lvl) {
+        const int shf = max(pos - 8, 0);
+        uint32_t* h = sh.hist + 256 * lvl;
+        const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
+#pragma unroll
+        for (int q = 0; q < kSamples; ++q) {
+          const uint32_t off = smp[q] - mn;
+          if (smp[q] != kKeyNegInf && ((off ^ pre) & fixed) == 0)
+            atomicAdd(&h[(off >> shf) & 255u], 1u);
+        }
+        __syncthreads();
+        const BinPick b = pick_bin256(h, need);
+        need -= b.above;
+        acc += b.above;
+        got = acc + b.count;                  // sample keys >= the bin's lower edge
+        pre |= b.bin << shf;
+        pos = shf;
+      }
+      T = mn + pre;
+    }
+
+    // ---- the list: every key >= T with its column, the row's candidates and
+    // its largest key.  A wave counts its keys >= T, reserves their slots with
+    // one LDS atomic and writes them (ballot offsets); a wave whose keys do not
+    // fit writes none (the list then overflows and the full selection runs).
+    uint32_t wcnt = 0, wcand = 0, lmax = 0;
 #pragma unroll
     for (int m = 0; m < kTiles; ++m)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        atomicAdd(&h[k[m][u] != kKeyNegInf ? (k[m][u] >> 21) : 2048u], 1u);
-  }
-  __syncthreads();
-  uint32_t n_cand;
-  {
-    uint32_t local = 0;
-    for (int b = t; b < 2048; b += kTopkThreads) {
-      const uint32_t c = sh.hist[b] + hist_more[b] + hist_more[kHistStride + b] +
-                         hist_more[2 * kHistStride + b];
-      local += c;
-      sh.hist[b] = c;                         // copy 0 becomes the folded histogram
+      for (int u = 0; u < 4; ++u) {
+        lmax = max(lmax, k[m][u]);
+        wcnt += __popcll(__ballot(k[m][u] >= T));
+        wcand += __popcll(__ballot(k[m][u] != kKeyNegInf));
+      }
+    // the counts are formed here, not where they are used (their 32 masks
+    // would stay live through the writes)
+    asm volatile("" : "+s"(wcnt), "+s"(wcand));
+    const bool t_ok = T > kKeyNegInf;
+    uint32_t base = 0;
+    if (t_ok && lane == 0) base = atomicAdd(&list_count, wcnt);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+    if (t_ok && base + wcnt <= (uint32_t)kCap) {
+      // The compares are made again here: kept from the counting pass, their
+      // masks (two scalar registers per key) would not fit.
+      uint32_t T2 = T;
+      asm volatile("" : "+s"(T2));
+      uint32_t run = base;
+#pragma unroll
+      for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t key = k[m][u];
+          const bool pass = key >= T2;
+          const uint64_t b = __ballot(pass);
+          if (pass) {
+            const uint32_t off =
+                run + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            bin_keys[off] = key;
+            list_col[off] = (uint16_t)(m * kTile + 4 * t + u);
+          }
+          run += __popcll(b);
+        }
     }
-    block_exclusive_scan<uint32_t>(local, sh.wave_sums32, &n_cand);
+    lmax = wave_max_u32(lmax);
+    if (lane == 0) {
+      list_stat[0][wave] = wcand;
+      list_stat[1][wave] = lmax;
+    }
+    __syncthreads();
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readfirstlane((int)list_count);
+    const uint32_t n_cand = wave_sum_u32(wl ? list_stat[0][lane] : 0u);
+    const uint32_t M = wave_max_u32(wl ? list_stat[1][lane] : 0u);
+    take_all = n_cand <= (uint32_t)p.topk;
+    fast = !take_all && t_ok && total >= (uint32_t)p.topk && total <= (uint32_t)kCap;
+
+    if (fast) {
+      // ---- radix levels over the list, on the bits where T and M differ ----
+      uint32_t need = (uint32_t)p.topk;
+      int pos = 32 - __clz(M ^ T);
+      uint32_t prefix = pos >= 32 ? 0u : M & (~0u << pos);
+      bool whole = false;
+      for (int lvl = 0; pos > 0; ++lvl) {
+        const int shf = max(pos - 8, 0);
+        uint32_t* h = sh.hist + 1024 + 256 * lvl;
+        const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
+        for (int i = t; i < (int)total; i += kTopkThreads) {
+          const uint32_t key = bin_keys[i];
+          if (((key ^ prefix) & fixed) == 0) atomicAdd(&h[(key >> shf) & 255u], 1u);
+        }
+        __syncthreads();
+        const BinPick b = pick_bin256(h, need);
+        need -= b.above;
+        prefix |= b.bin << shf;
+        pos = shf;
+        if (pos > 0 && b.count == need && prefix != 0) {   // the whole bin is taken
+          whole = true;
+          break;
+        }
+      }
+      K = whole ? prefix - 1u : prefix;
+      need_eq = whole ? 0u : need;
+      for (int i = t; i < (int)total; i += kTopkThreads) {
+        const uint32_t key = bin_keys[i];
+        const int c = list_col[i];
+        if (key > K) atomicOr(&gmap[c >> 5], 1u << (c & 31));
+        else if (key == K) atomicOr(&qmap[c >> 5], 1u << (c & 31));
+      }
+    }
   }
 
-  // keys > K are taken, then the first need_eq keys equal to K in column order
-  uint32_t K = 0, need_eq = 0;
-  const bool take_all = n_cand <= (uint32_t)p.topk;
-  if (!take_all) {
-    uint32_t need = (uint32_t)p.topk;
-    find_bin(sh, 2048, need);
-    const uint32_t in_bin = sh.hist[sh.sel_bin];
-    need -= sh.sel_above;
-    uint32_t prefix = sh.sel_bin << 21, mask = 2047u << 21;
-    __syncthreads();
-    bool whole_bin = in_bin == need && prefix != 0;
-    if (!whole_bin) {
-      const bool listed = in_bin <= (uint32_t)kTopkCap;
-      if (listed) {                           // gather the bin's keys
+  if (!fast) {
+    if (!take_all) {
+      // ---- first level: every key, no branch; -inf counts into a spare slot --
+      // Each quarter of a wave counts into its own copy of the histogram (most
+      // keys fall in a few bins), folded before the search.
+      const int copy = lane >> 4;
+      for (int b = t; b < kHistStride; b += kTopkThreads) sh.hist[b] = 0;
+      for (int b = t; b < 3 * kHistStride; b += kTopkThreads) hist_more[b] = 0;
+      if (t == 0) bin_count = 0;
+      __syncthreads();
+      {
+        uint32_t* h = copy > 0 ? hist_more + (copy - 1) * kHistStride : sh.hist;
 #pragma unroll
         for (int m = 0; m < kTiles; ++m)
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            if (k[m][u] != kKeyNegInf && (k[m][u] & mask) == prefix) {
-              const uint32_t slot = atomicAdd(&bin_count, 1u);
-              if (slot < (uint32_t)kTopkCap) bin_keys[slot] = k[m][u];
-            }
-        __syncthreads();
+            atomicAdd(&h[k[m][u] != kKeyNegInf ? (k[m][u] >> 21) : 2048u], 1u);
       }
-      constexpr int kShift[3] = {21, 10, 0};
-      constexpr int kBins[3] = {2048, 2048, 1024};
-#pragma unroll
-      for (int lvl = 1; lvl < 3; ++lvl) {
-        for (int b = t; b < kBins[lvl]; b += kTopkThreads) sh.hist[b] = 0;
-        __syncthreads();
-        if (listed) {
-          for (int i = t; i < (int)in_bin; i += kTopkThreads) {
-            const uint32_t key = bin_keys[i];
-            if ((key & mask) == prefix)
-              atomicAdd(&sh.hist[(key >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < kTiles; ++m)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (k[m][u] != kKeyNegInf && (k[m][u] & mask) == prefix)
-                atomicAdd(&sh.hist[(k[m][u] >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
+      __syncthreads();
+      uint32_t n_cand;
+      {
+        uint32_t local = 0;
+        for (int b = t; b < 2048; b += kTopkThreads) {
+          const uint32_t c = sh.hist[b] + hist_more[b] + hist_more[kHistStride + b] +
+                             hist_more[2 * kHistStride + b];
+          local += c;
+          sh.hist[b] = c;                     // copy 0 becomes the folded histogram
         }
-        __syncthreads();
-        find_bin(sh, kBins[lvl], need);
+        block_exclusive_scan<uint32_t>(local, sh.wave_sums32, &n_cand);
+      }
+      take_all = n_cand <= (uint32_t)p.topk;
+      if (!take_all) {
+        uint32_t need = (uint32_t)p.topk;
+        find_bin(sh, 2048, need);
+        const uint32_t in_bin = sh.hist[sh.sel_bin];
         need -= sh.sel_above;
-        const uint32_t c = sh.hist[sh.sel_bin];
-        prefix |= sh.sel_bin << kShift[lvl];
-        mask |= (uint32_t)(kBins[lvl] - 1) << kShift[lvl];
+        uint32_t prefix = sh.sel_bin << 21, mask = 2047u << 21;
         __syncthreads();
-        if (c == need && lvl == 1 && prefix != 0) {   // the whole finer bin is taken
-          whole_bin = true;
-          break;
+        bool whole_bin = in_bin == need && prefix != 0;
+        if (!whole_bin) {
+          const bool listed = in_bin <= (uint32_t)kCap;
+          if (listed) {                       // gather the bin's keys
+#pragma unroll
+            for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (k[m][u] != kKeyNegInf && (k[m][u] & mask) == prefix) {
+                  const uint32_t slot = atomicAdd(&bin_count, 1u);
+                  if (slot < (uint32_t)kCap) bin_keys[slot] = k[m][u];
+                }
+            __syncthreads();
+          }
+          constexpr int kShift[3] = {21, 10, 0};
+          constexpr int kBins[3] = {2048, 2048, 1024};
+#pragma unroll
+          for (int lvl = 1; lvl < 3; ++lvl) {
+            for (int b = t; b < kBins[lvl]; b += kTopkThreads) sh.hist[b] = 0;
+            __syncthreads();
+            if (listed) {
+              for (int i = t; i < (int)in_bin; i += kTopkThreads) {
+                const uint32_t key = bin_keys[i];
+                if ((key & mask) == prefix)
+                  atomicAdd(&sh.hist[(key >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
+              }
+            } else {
+#pragma unroll
+              for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                  if (k[m][u] != kKeyNegInf && (k[m][u] & mask) == prefix)
+                    atomicAdd(&sh.hist[(k[m][u] >> kShift[lvl]) & (kBins[lvl] - 1)], 1u);
+            }
+            __syncthreads();
+            find_bin(sh, kBins[lvl], need);
+            need -= sh.sel_above;
+            const uint32_t c = sh.hist[sh.sel_bin];
+            prefix |= sh.sel_bin << kShift[lvl];
+            mask |= (uint32_t)(kBins[lvl] - 1) << kShift[lvl];
+            __syncthreads();
+            if (c == need && lvl == 1 && prefix != 0) {   // the whole finer bin is taken
+              whole_bin = true;
+              break;
+            }
+          }
         }
+        K = whole_bin ? prefix - 1u : prefix;
+        need_eq = whole_bin ? 0u : need;
       }
     }
-    K = whole_bin ? prefix - 1u : prefix;
-    need_eq = whole_bin ? 0u : need;
+    // ---- the selection's bitmaps from the registers -------------------------
+    for (int w = t; w < 2 * kWords; w += kTopkThreads) u_.maps[w] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m) {
+      uint32_t ng = 0, nq = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool valid = k[m][u] != kKeyNegInf;
+        ng |= (valid && k[m][u] > K) ? 1u << u : 0u;
+        nq |= (valid && k[m][u] == K) ? 1u << u : 0u;
+      }
+      const int c = m * kTile + 4 * t;        // the 4 columns' word and bit
+      if (ng) atomicOr(&gmap[c >> 5], ng << (c & 31));
+      if (nq) atomicOr(&qmap[c >> 5], nq << (c & 31));
+    }
   }
-  const uint32_t n_sel = take_all ? n_cand : (uint32_t)p.topk;
+  __syncthreads();
 
   // ---- ordered write ---------------------------------------------------------
-  // Bitmaps over the row's columns: gmap (key > K) and qmap (key == K).  The
-  // block then walks them one 32-column word at a time in column order: a
-  // scan of the words' counts gives each word's first output slot and how
-  // many of its == K columns are still taken (the first need_eq in column
-  // order); each word's columns are written in ascending order.
-  for (int w = t; w < 2 * kWords; w += kTopkThreads) u_.maps[w] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < kTiles; ++m) {
-    uint32_t ng = 0, nq = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool valid = k[m][u] != kKeyNegInf;
-      ng |= (valid && k[m][u] > K) ? 1u << u : 0u;
-      nq |= (valid && k[m][u] == K) ? 1u << u : 0u;
-    }
-    const int c = m * kTile + 4 * t;          // the 4 columns' word and bit
-    if (ng) atomicOr(&gmap[c >> 5], ng << (c & 31));
-    if (nq) atomicOr(&qmap[c >> 5], nq << (c & 31));
-  }
-  __syncthreads();
+  // The block walks the bitmaps gmap (key > K) and qmap (key == K) one
+  // 32-column word at a time in column order: a scan of the words' counts
+  // gives each word's first output slot and how many of its == K columns are
+  // still taken (the first need_eq in column order); each word's columns are
+  // written in ascending order.
   constexpr int kWpt = (kWords + kTopkThreads - 1) / kTopkThreads;   // per thread
   uint32_t wg[kWpt], wq[kWpt];
   uint32_t cg = 0, cq = 0;
@@ -548,6 +802,10 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   const uint64_t before =
       block_exclusive_scan<uint64_t>(((uint64_t)cq << 32) | cg, sh.wave_sums64, &total);
   uint32_t gb = (uint32_t)before, qb = (uint32_t)(before >> 32);
+  // columns written: all keys > K, then need_eq of the == K ones (topk, or
+  // every candidate when all are taken)
+  const uint32_t n_sel =
+      min((uint32_t)p.topk, (uint32_t)total + min(need_eq, (uint32_t)(total >> 32)));
 #pragma unroll
   for (int j = 0; j < kWpt; ++j) {
     // the == K columns of this word still taken: the lowest `take` set bits

@@ -151,3 +151,47 @@ def test_topk_bf16_last_column_of_an_odd_row(skv):
     for k in (1, min(skv, 5)):
         got = mq.mqa_logits_topk(t, k).cpu().numpy()
         assert np.array_equal(got, oracle.topk_indices(xb, k)), f"k={k}"
+
+
+def _prefilter_rows(skv, rng):
+    """Rows that lead the register kernel's sampled-threshold prefilter into
+    each of its outcomes: taken (plain noise), a wave's list segment
+    overflowing (the largest keys all in the columns one wave holds), the
+    whole list overflowing (the largest keys only in columns the sample does
+    not read), too few keys at or above the threshold (mostly -inf rows), a
+    threshold among negative values (topk near half the row), one huge
+    outlier (the radix window spans every key bit), and every key equal."""
+    cols = np.arange(skv)
+    noise = rng.standard_normal((8, skv))
+    x = noise.copy()
+    x[1, (cols % 4096) < 256] += 50.0              # thread 0..63's columns: wave 0's
+    x[2, (cols % 4) == 1] += 50.0                  # the sample reads columns 4t only
+    x[3, rng.random(skv) < 0.9] = -np.inf
+    x[4] = -np.abs(noise[4]) - 1.0                 # all negative
+    x[5, skv // 3] = 3.0e38
+    x[6] = 0.75
+    x[7] = np.round(noise[7] * 4) / 4              # coarse grid: wide ties at the cut
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("skv", [6000, 12000, 32768, 65536])
+@pytest.mark.parametrize("topk", [1, 2048, 2560, 2561, 4096])
+def test_topk_prefilter_outcomes(skv, topk):
+    # every outcome must give the oracle's selection bit for bit, whichever
+    # path the kernel took (topk 2560 is the largest the 32-key kernels
+    # prefilter, 4096 the 64-key kernel's)
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(skv + topk)
+    x = _prefilter_rows(skv, rng)
+    log(f"[topk] prefilter outcomes Skv={skv} topk={topk}")
+    for bf16 in (False, True):
+        xs = x
+        t = dev(x)
+        if bf16:
+            bits = synth.encode_bf16(x)
+            xs = synth.decode_bf16(bits).reshape(x.shape)
+            t = dev(bits.view(np.int16)).view(torch.bfloat16)
+        got = mq.mqa_logits_topk(t, topk).cpu().numpy()
+        want = oracle.topk_indices(xs, topk, None, None)
+        for r in range(x.shape[0]):
+            assert np.array_equal(got[r], want[r]), f"row {r} bf16={bf16}"
