@@ -349,9 +349,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       kk[u] = c + u < n ? src.key(c + u) : kKeyNegInf;
+      // every candidate when all are taken (a NaN with all bits set has key 0)
       const bool valid = kk[u] != kKeyNegInf;
-      g += (valid && kk[u] > K) ? 1u : 0u;
-      q += (valid && kk[u] == K) ? 1u : 0u;
+      g += (valid && (take_all || kk[u] > K)) ? 1u : 0u;
+      q += (valid && !take_all && kk[u] == K) ? 1u : 0u;
     }
     uint64_t tile_total;
     const uint64_t before =
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool valid = kk[u] != kKeyNegInf;
-      if (valid && kk[u] > K) {
+      if (valid && (take_all || kk[u] > K)) {
         const uint32_t pos = gb + min(qb, need_eq);
         if (pos < (uint32_t)p.topk) out[pos] = s + c + u;
         ++gb;
@@ -770,9 +771,10 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
       uint32_t ng = 0, nq = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        // every candidate when all are taken (a NaN with all bits set has key 0)
         const bool valid = k[m][u] != kKeyNegInf;
-        ng |= (valid && k[m][u] > K) ? 1u << u : 0u;
-        nq |= (valid && k[m][u] == K) ? 1u << u : 0u;
+        ng |= (valid && (take_all || k[m][u] > K)) ? 1u << u : 0u;
+        nq |= (valid && !take_all && k[m][u] == K) ? 1u << u : 0u;
       }
       const int c = m * kTile + 4 * t;        // the 4 columns' word and bit
       if (ng) atomicOr(&gmap[c >> 5], ng << (c & 31));

@@ -195,3 +195,27 @@ def test_topk_prefilter_outcomes(skv, topk):
         want = oracle.topk_indices(xs, topk, None, None)
         for r in range(x.shape[0]):
             assert np.array_equal(got[r], want[r]), f"row {r} bf16={bf16}"
+
+
+@pytest.mark.parametrize("skv", [100, 3000, 70000])
+def test_topk_takes_every_candidate_including_nan_bit_patterns(skv):
+    # rows with at most topk candidates take all of them: every column that
+    # is not -inf, NaN bit patterns included (the order is IEEE 754 total
+    # order of the bit patterns, where a NaN is not -inf), ascending, then -1
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(skv)
+    bits = rng.standard_normal((4, skv)).astype(np.float32).view(np.uint32)
+    nan_patterns = np.array([0x7FC00000, 0xFFC00000, 0xFFFFFFFF, 0x7FFFFFFF, 0xFF800001],
+                            np.uint32)
+    for r in range(4):
+        cols = rng.choice(skv, size=min(skv, 5), replace=False)
+        bits[r, cols] = nan_patterns[:cols.size]
+    bits[:, rng.random(skv) < 0.3] = np.float32(-np.inf).view(np.uint32)
+    topk = skv                                      # every row takes all its candidates
+    log(f"[topk] take-all with NaN bit patterns Skv={skv}")
+    got = mq.mqa_logits_topk(dev(bits.view(np.float32)), topk).cpu().numpy()
+    neg_inf = np.float32(-np.inf).view(np.uint32)
+    for r in range(4):
+        want = np.nonzero(bits[r] != neg_inf)[0]
+        assert np.array_equal(got[r, :want.size], want), f"row {r}"
+        assert np.all(got[r, want.size:] == -1), f"row {r} padding"
