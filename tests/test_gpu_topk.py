@@ -219,3 +219,65 @@ def test_topk_takes_every_candidate_including_nan_bit_patterns(skv):
         want = np.nonzero(bits[r] != neg_inf)[0]
         assert np.array_equal(got[r, :want.size], want), f"row {r}"
         assert np.all(got[r, want.size:] == -1), f"row {r} padding"
+
+
+def _values(rng, kind, shape):
+    """Ten value distributions for the top-k: normal, exponential, integers
+    (heavy ties), lognormal (wide range), normal with +-1e30 outliers, a
+    narrow all-negative band, a coarse grid, four distinct values with both
+    zeros, tiny (subnormal-scale) values, and two far-apart clusters."""
+    if kind == 0:
+        return rng.standard_normal(shape)
+    if kind == 1:
+        return rng.exponential(1.0, shape)
+    if kind == 2:
+        return rng.integers(-5, 6, shape).astype(np.float64)
+    if kind == 3:
+        return rng.lognormal(0.0, 2.0, shape)
+    if kind == 4:
+        x = rng.standard_normal(shape)
+        x[rng.random(shape) < 0.001] = 1e30
+        x[rng.random(shape) < 0.001] = -1e30
+        return x
+    if kind == 5:
+        return -np.abs(rng.standard_normal(shape)) * 1e-3 - 7.0
+    if kind == 6:
+        return np.round(rng.standard_normal(shape) * 2) / 2
+    if kind == 7:
+        return rng.choice([0.0, -0.0, 1.0, 2.0], size=shape)
+    if kind == 8:
+        return rng.standard_normal(shape) * 1e-30
+    return np.where(rng.random(shape) < 0.5, rng.standard_normal(shape) + 100,
+                    rng.standard_normal(shape) - 100)
+
+
+@pytest.mark.parametrize("kind", range(10))
+def test_topk_value_distributions(kind):
+    # the selection's thresholds and radix windows depend on the values'
+    # spread, ties and signs; each distribution runs six seeded cases with
+    # drawn row lengths (every kernel size), topk (around the prefilter's
+    # limits), -inf holes, ranges and logits types
+    import mqa_logits_amd as mq
+    for case in range(6):
+        rng = np.random.default_rng([kind, case, 77])
+        sq = int(rng.integers(1, 9))
+        skv = int(rng.choice([int(rng.integers(1, 9000)), int(rng.integers(9000, 33000)),
+                              int(rng.integers(33000, 65537)), int(rng.integers(65537, 80000))]))
+        topk = int(rng.choice([1, int(rng.integers(1, 2600)), 2048, 2560, 2561, 4096]))
+        x = _values(rng, kind, (sq, skv))
+        x[rng.random((sq, skv)) < rng.choice([0.0, 0.05, 0.5, 0.95])] = -np.inf
+        x = x.astype(np.float32)
+        ks = ke = None
+        if rng.random() < 0.5:
+            ks = rng.integers(-10, skv, sq).astype(np.int32)
+            ke = (ks + rng.integers(-5, skv + 10, sq)).astype(np.int32)
+        t = dev(x)
+        bf16 = bool(rng.random() < 0.3)
+        if bf16:
+            bits = synth.encode_bf16(x)
+            x = synth.decode_bf16(bits).reshape(x.shape)
+            t = dev(bits.view(np.int16)).view(torch.bfloat16)
+        what = f"kind {kind} case {case} Sq={sq} Skv={skv} topk={topk} bf16={bf16}"
+        log(f"[topk] {what}")
+        got = mq.mqa_logits_topk(t, topk, dev(ks), dev(ke)).cpu().numpy()
+        assert np.array_equal(got, oracle.topk_indices(x, topk, ks, ke)), what
