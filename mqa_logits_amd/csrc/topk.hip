@@ -22,6 +22,8 @@
 //   * Otherwise every level is a pass over the row, and a last pass writes
 //     the selected columns in column order with a block-wide prefix count of
 //     (keys > K, keys == K).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,6 +32,7 @@ namespace mqa {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWaveLanes;
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;       // key of -inf: not a candidate
+constexpr uint32_t kBitsNegInf = 0xFF800000u;      // fp32 bits of -inf
 
 // Order-preserving key of an fp32 bit pattern: larger float, larger key.
 __device__ __forceinline__ uint32_t order_key(uint32_t bits) {
@@ -52,9 +55,10 @@ struct TopkRow {
     }
     return order_key(bits);
   }
-  // Keys of columns s + c .. s + c + 3 (one 8- or 16-byte load); columns at or
-  // past n (the range end, relative) are -inf.
-  __device__ __forceinline__ void key4(int c, int n, uint32_t (&k)[4]) const {
+  // fp32 bit patterns of columns s + c .. s + c + 3 (one 8- or 16-byte load);
+  // columns at or past n (the range end, relative) read as -inf unless the
+  // caller knows all four are in range (`full`).
+  __device__ __forceinline__ void bits4(int c, int n, bool full, uint32_t (&b)[4]) const {
     uint32_t bits[4];
     if constexpr (IN == kBF16) {
       typedef int v2i __attribute__((ext_vector_type(2)));
@@ -75,9 +79,54 @@ struct TopkRow {
       for (int u = 0; u < 4; ++u) bits[u] = (uint32_t)w[u];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) k[u] = c + u < n ? order_key(bits[u]) : kKeyNegInf;
+    for (int u = 0; u < 4; ++u) b[u] = full || c + u < n ? bits[u] : kBitsNegInf;
   }
 };
+
+// ---- wave-level scans and reductions ----------------------------------------
+// Inclusive scans over the wave with DPP moves (ALU latency, no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16, then row 0's
+// and row 1's last lanes broadcast to the rows after them.  `id` is the
+// operation's identity, which lanes without a source contribute.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x, uint32_t id, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+struct OpAdd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+struct OpMin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, 0u, OpMax{}), kWaveLanes - 1);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, ~0u, OpMin{}), kWaveLanes - 1);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, 0u, OpAdd{}), kWaveLanes - 1);
+}
+
+// Inclusive sum over the wave; a 64-bit value is a pair of 32-bit counts
+// (high, low) that never carry into each other, scanned as two.  Every lane
+// of the wave takes part.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  return wave_scan_u32(x, 0u, OpAdd{});
+}
+__device__ __forceinline__ uint64_t wave_incl_sum(uint64_t x) {
+  return ((uint64_t)wave_scan_u32((uint32_t)(x >> 32), 0u, OpAdd{}) << 32) |
+         wave_scan_u32((uint32_t)x, 0u, OpAdd{});
+}
 
 // Exclusive prefix sum over the block (thread order) of a per-thread value;
 // *total receives the block total.  Every thread must call it.
@@ -85,21 +134,12 @@ template <class T>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* wave_sums, T* total) {
   const int lane = threadIdx.x & (kWaveLanes - 1);
   const int wave = threadIdx.x >> 6;
-  T x = v;
-#pragma unroll
-  for (int o = 1; o < kWaveLanes; o <<= 1) {
-    const T y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const T x = wave_incl_sum(v);
   if (lane == kWaveLanes - 1) wave_sums[wave] = x;
   __syncthreads();
   if (wave == 0) {
     T w = lane < kTopkWaves ? wave_sums[lane] : T(0);
-#pragma unroll
-    for (int o = 1; o < kTopkWaves; o <<= 1) {
-      const T y = __shfl_up(w, o);
-      if (lane >= o) w += y;
-    }
+    w = wave_incl_sum(w);
     if (lane < kTopkWaves) wave_sums[lane] = w;             // inclusive per wave
   }
   __syncthreads();
@@ -378,40 +418,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
   for (int pos = (int)n_sel + t; pos < p.topk; pos += kTopkThreads) out[pos] = -1;
 }
 
-// ---- wave-level helpers of the register kernel's prefilter ------------------
-// Inclusive scans over the wave with DPP moves (ALU latency, no LDS round
-// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16, then row 0's
-// and row 1's last lanes broadcast to the rows after them.  `id` is the
-// operation's identity, which lanes without a source contribute.
-template <class Op>
-__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x, uint32_t id, Op op) {
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
-  return x;
-}
-struct OpAdd {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
-};
-struct OpMax {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
-};
-struct OpMin {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
-};
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, 0u, OpMax{}), kWaveLanes - 1);
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, ~0u, OpMin{}), kWaveLanes - 1);
-}
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, 0u, OpAdd{}), kWaveLanes - 1);
-}
-
 // One radix level over a 256-bin histogram h (bin 255 holds the largest
 // keys): the bin holding the need-th largest key, the count in higher bins
 // and the bin's own count.  Every wave reads the histogram and reaches the
@@ -485,8 +491,8 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   uint32_t* const hist_more = u_.hist_more;
   uint32_t* const gmap = u_.maps;
   uint32_t* const qmap = u_.maps + kWords;
-  __shared__ uint32_t bin_keys[kCap];         // the prefilter's keys, or the first-level bin's
-  __shared__ uint16_t list_col[kCap];         // the prefilter's columns (range-relative)
+  __shared__ uint2 list_kc[kCap];             // the prefilter's (bit pattern, column) pairs
+  uint32_t* const bin_keys = reinterpret_cast<uint32_t*>(list_kc);   // or the first-level bin's keys
   __shared__ uint32_t smp_stat[3][kTopkWaves];
   __shared__ uint32_t list_stat[2][kTopkWaves];
   __shared__ uint32_t list_count;
@@ -507,9 +513,12 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
                         s, p.skv - 1 - s};
   int32_t* out = p.indices + row * p.out_stride;
 
+  // The row's fp32 bit patterns, -inf past the range (only a tile the range
+  // ends in is checked); the prefilter compares them as they are, the other
+  // paths turn them into keys first.
   uint32_t k[kTiles][4];
 #pragma unroll
-  for (int m = 0; m < kTiles; ++m) src.key4(m * kTile + 4 * t, n, k[m]);
+  for (int m = 0; m < kTiles; ++m) src.bits4(m * kTile + 4 * t, n, (m + 1) * kTile <= n, k[m]);
 
   // keys > K are taken, then the first need_eq keys equal to K in column order
   uint32_t K = 0, need_eq = 0;
@@ -529,6 +538,7 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
       uint32_t v = k[0][0];
 #pragma unroll
       for (int m = 1; m < kTiles; ++m) v = tq == m ? k[m][0] : v;
+      v = order_key(v);
       smp[q] = v;
       const bool valid = v != kKeyNegInf;     // columns past the range hold -inf keys
       vmin = valid ? min(vmin, v) : vmin;
@@ -588,69 +598,94 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
     // its largest key.  A wave counts its keys >= T, reserves their slots with
     // one LDS atomic and writes them (ballot offsets); a wave whose keys do not
     // fit writes none (the list then overflows and the full selection runs).
-    uint32_t wcnt = 0, wcand = 0, lmax = 0;
-#pragma unroll
-    for (int m = 0; m < kTiles; ++m)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        lmax = max(lmax, k[m][u]);
-        wcnt += __popcll(__ballot(k[m][u] >= T));
-        wcand += __popcll(__ballot(k[m][u] != kKeyNegInf));
-      }
-    // the counts are formed here, not where they are used (their 32 masks
-    // would stay live through the writes)
-    asm volatile("" : "+s"(wcnt), "+s"(wcand));
+    // The compares run on the raw bit patterns: for T at or above +0, key >= T
+    // exactly when the bits as a signed integer reach T's; for T below -0,
+    // exactly when the bits as an unsigned integer are at most T's (every
+    // non-negative value, and the negative ones nearer zero).  The row's
+    // largest key is bounded by its largest bits as a signed integer (its
+    // largest non-negative value), or by -0 when every value is negative.
     const bool t_ok = T > kKeyNegInf;
-    uint32_t base = 0;
-    if (t_ok && lane == 0) base = atomicAdd(&list_count, wcnt);
-    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-    if (t_ok && base + wcnt <= (uint32_t)kCap) {
-      // The compares are made again here: kept from the counting pass, their
-      // masks (two scalar registers per key) would not fit.
-      uint32_t T2 = T;
-      asm volatile("" : "+s"(T2));
-      uint32_t run = base;
+    const bool t_pos = T >= 0x80000000u;
+    uint32_t wcnt = 0, wcand = 0;
+    int32_t lmax = INT32_MIN;
+    auto count_and_list = [&](auto pos_tag) {
+      constexpr bool kPos = decltype(pos_tag)::value;
+      const uint32_t tb = kPos ? T ^ 0x80000000u : ~T;
+      auto passes = [](uint32_t bits, uint32_t thr) {
+        return kPos ? (int32_t)bits >= (int32_t)thr : bits <= thr;
+      };
 #pragma unroll
       for (int m = 0; m < kTiles; ++m)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t key = k[m][u];
-          const bool pass = key >= T2;
-          const uint64_t b = __ballot(pass);
-          if (pass) {
-            const uint32_t off =
-                run + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-            bin_keys[off] = key;
-            list_col[off] = (uint16_t)(m * kTile + 4 * t + u);
-          }
-          run += __popcll(b);
+          lmax = max(lmax, (int32_t)k[m][u]);
+          wcnt += __popcll(__ballot(passes(k[m][u], tb)));
+          wcand += __popcll(__ballot(k[m][u] != kBitsNegInf));
         }
-    }
-    lmax = wave_max_u32(lmax);
+      // the counts are formed here, not where they are used (their 32 masks
+      // would stay live through the writes)
+      asm volatile("" : "+s"(wcnt), "+s"(wcand));
+      uint32_t base = 0;
+      if (t_ok && lane == 0) base = atomicAdd(&list_count, wcnt);
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+      if (t_ok && base + wcnt <= (uint32_t)kCap) {
+        // The compares are made again here: kept from the counting pass, their
+        // masks (two scalar registers per key) would not fit.
+        uint32_t tb2 = tb;
+        asm volatile("" : "+s"(tb2));
+        // the columns are formed again here too (kept from the range checks
+        // of the loads, 32 of them would stay live)
+        uint32_t col4 = 4 * t;
+        asm volatile("" : "+v"(col4));
+        uint32_t run = base;
+#pragma unroll
+        for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool pass = passes(k[m][u], tb2);
+            const uint64_t b = __ballot(pass);
+            if (pass) {
+              const uint32_t off =
+                  run + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+              // a copy made here: paired with its column for the 8-byte
+              // store, the key itself would take a register pair for its
+              // whole life
+              uint32_t kv = k[m][u];
+              asm volatile("" : "+v"(kv));
+              list_kc[off] = make_uint2(kv, col4 + (uint32_t)(m * kTile + u));
+            }
+            run += __popcll(b);
+          }
+      }
+    };
+    if (t_pos) count_and_list(std::true_type{});
+    else count_and_list(std::false_type{});
+    const uint32_t wmax = wave_max_u32((uint32_t)lmax ^ 0x80000000u);   // signed order
     if (lane == 0) {
       list_stat[0][wave] = wcand;
-      list_stat[1][wave] = lmax;
+      list_stat[1][wave] = wmax;
     }
     __syncthreads();
     const uint32_t total = (uint32_t)__builtin_amdgcn_readfirstlane((int)list_count);
     const uint32_t n_cand = wave_sum_u32(wl ? list_stat[0][lane] : 0u);
-    const uint32_t M = wave_max_u32(wl ? list_stat[1][lane] : 0u);
+    const int32_t max_bits = (int32_t)(wave_max_u32(wl ? list_stat[1][lane] : 0u) ^ 0x80000000u);
+    const uint32_t U = max_bits >= 0 ? (uint32_t)max_bits | 0x80000000u : 0x7FFFFFFFu;
     take_all = n_cand <= (uint32_t)p.topk;
     fast = !take_all && t_ok && total >= (uint32_t)p.topk && total <= (uint32_t)kCap;
 
     if (fast) {
-      // ---- radix levels over the list, on the bits where T and M differ ----
+      // ---- radix levels over the list, on the bits where T and U differ ----
       uint32_t need = (uint32_t)p.topk;
-      int pos = 32 - __clz(M ^ T);
-      uint32_t prefix = pos >= 32 ? 0u : M & (~0u << pos);
+      int pos = 32 - __clz(U ^ T);
+      uint32_t prefix = pos >= 32 ? 0u : U & (~0u << pos);
       bool whole = false;
       for (int lvl = 0; pos > 0; ++lvl) {
         const int shf = max(pos - 8, 0);
         uint32_t* h = sh.hist + 1024 + 256 * lvl;
         const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
         for (int i = t; i < (int)total; i += kTopkThreads) {
-          const uint32_t key = bin_keys[i];
+          const uint32_t key = order_key(list_kc[i].x);
           if (((key ^ prefix) & fixed) == 0) atomicAdd(&h[(key >> shf) & 255u], 1u);
         }
         __syncthreads();
@@ -666,8 +701,9 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
       K = whole ? prefix - 1u : prefix;
       need_eq = whole ? 0u : need;
       for (int i = t; i < (int)total; i += kTopkThreads) {
-        const uint32_t key = bin_keys[i];
-        const int c = list_col[i];
+        const uint2 e = list_kc[i];
+        const uint32_t key = order_key(e.x);
+        const int c = (int)e.y;
         if (key > K) atomicOr(&gmap[c >> 5], 1u << (c & 31));
         else if (key == K) atomicOr(&qmap[c >> 5], 1u << (c & 31));
       }
@@ -675,6 +711,11 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   }
 
   if (!fast) {
+    // keys for the full selection and the take-all marks
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) k[m][u] = order_key(k[m][u]);
     if (!take_all) {
       // ---- first level: every key, no branch; -inf counts into a spare slot --
       // Each quarter of a wave counts into its own copy of the histogram (most
