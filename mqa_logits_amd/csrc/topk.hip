@@ -9,9 +9,12 @@
 // order and padded with -1 when a row has fewer than topk candidates.
 //
 // One block of 1024 threads per row.  Logits map to order-preserving 32-bit
-// keys (sign-magnitude to two's-complement order) and a radix select over
-// them (11 + 11 + 10 bits, one LDS histogram per level) finds the topk-th
-// largest key K and how many keys equal to K to keep.
+// keys (sign-magnitude to two's-complement order); the selection is the
+// topk-th largest key K and how many keys equal to K to keep.  Rows of up to
+// 65536 columns are held in registers (topk_reg_kernel below: a sampled
+// threshold narrows the row to a short LDS list first).  Longer rows stream
+// (topk_stream_kernel), with a radix select over the keys (11 + 11 + 10
+// bits, one LDS histogram per level):
 //   * A first pass over the row builds the top-11-bit histogram: the bin B of
 //     the topk-th key, the count above it and the count in it.
 //   * When both counts fit in LDS (the usual case) a second pass copies, in
