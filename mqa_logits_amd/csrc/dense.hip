@@ -1,6 +1,8 @@
 // Dense and compressed weighted MQA logits for gfx950: fp32-logits instances
 // split by row chunks, the dispatch over logits type and work split, and the
 // compressed layout's row offsets.  The kernels are in dense_kernel.hpp.
+#include <type_traits>
+
 #include "dense_kernel.hpp"
 #include "schedule.hpp"
 
@@ -48,6 +50,29 @@ hipError_t launch_dense_metadata(const int32_t* ks, const int32_t* ke, int32_t s
   return hipGetLastError();
 }
 
+// Inclusive sum over the wave of a 64-bit value with DPP moves (ALU latency,
+// no LDS round trips): shifts by 1, 2, 4 and 8 lanes within each row of 16,
+// then row 0's and row 1's last lanes broadcast to the rows after them.  Each
+// 32-bit half moves on its own and the sum is formed in 64 bits; lanes
+// without a source add 0.  Every lane of the wave takes part.
+__device__ __forceinline__ int64_t wave_incl_sum_i64(int64_t x) {
+  auto step = [&](auto ctrl, auto row_mask) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, decltype(ctrl)::value,
+                                               decltype(row_mask)::value, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)x >> 32),
+                                               decltype(ctrl)::value, decltype(row_mask)::value,
+                                               0xf, false);
+    x += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  };
+  step(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});
+  step(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});
+  step(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});
+  step(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});
+  step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});
+  step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});
+  return x;
+}
+
 // Row offsets of the compressed layout: exclusive prefix sum of the clamped
 // row lengths, one block of 1024 threads walking the rows in chunks.
 __global__ __launch_bounds__(1024) void compressed_offsets_kernel(const int32_t* __restrict__ ks,
@@ -55,8 +80,8 @@ __global__ __launch_bounds__(1024) void compressed_offsets_kernel(const int32_t*
                                                                   int32_t sq, int32_t skv,
                                                                   int64_t* __restrict__ off) {
   // Thread t takes rows 4t .. 4t+3 of each round of 4096; a round is a scan
-  // of the threads' sums inside each wave (shuffles), then of the 16 wave
-  // totals, so it costs three barriers.
+  // of the threads' sums inside each wave, then of the 16 wave totals (both
+  // DPP scans), so it costs three barriers.
   constexpr int kPer = 4;
   constexpr int kWaves = 1024 / kWaveLanes;
   __shared__ int64_t wsum[kWaves];
@@ -74,21 +99,11 @@ __global__ __launch_bounds__(1024) void compressed_offsets_kernel(const int32_t*
       }
       tsum += len[k];
     }
-    int64_t x = tsum;                          // inclusive scan over the wave
-#pragma unroll
-    for (int d = 1; d < kWaveLanes; d <<= 1) {
-      const int64_t y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
+    const int64_t x = wave_incl_sum_i64(tsum);
     if (lane == kWaveLanes - 1) wsum[wave] = x;
     __syncthreads();
     if (wave == 0) {                           // inclusive scan of the wave totals
-      int64_t v = lane < kWaves ? wsum[lane] : 0;
-#pragma unroll
-      for (int d = 1; d < kWaves; d <<= 1) {
-        const int64_t y = __shfl_up(v, d);
-        if (lane >= d) v += y;
-      }
+      const int64_t v = wave_incl_sum_i64(lane < kWaves ? wsum[lane] : 0);
       if (lane < kWaves) wsum[lane] = v;
     }
     __syncthreads();
