@@ -205,12 +205,11 @@ __device__ __forceinline__ void find_bin(TopkShared& sh, int nbins, uint32_t nee
   __syncthreads();
 }
 
+// One row of any length, read from memory once per level (the streaming
+// selection); sh and ls are the block's LDS.  Every thread of the block calls it.
 template <int IN>
-__global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p) {
-  __shared__ TopkShared sh;
-  __shared__ TopkLists ls;
+__device__ void topk_stream_row(const TopkParams& p, int64_t row, TopkShared& sh, TopkLists& ls) {
   const int t = threadIdx.x;
-  const int64_t row = blockIdx.x;
   int s = 0, e = p.skv;
   if (p.k_start) {
     s = clampi(p.k_start[row], 0, p.skv);
@@ -421,6 +420,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
   for (int pos = (int)n_sel + t; pos < p.topk; pos += kTopkThreads) out[pos] = -1;
 }
 
+template <int IN>
+__global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p) {
+  __shared__ TopkShared sh;
+  __shared__ TopkLists ls;
+  topk_stream_row<IN>(p, blockIdx.x, sh, ls);
+}
+
 // One radix level over a 256-bin histogram h (bin 255 holds the largest
 // keys): the bin holding the need-th largest key, the count in higher bins
 // and the bin's own count.  Every wave reads the histogram and reaches the
@@ -453,38 +459,301 @@ __device__ __forceinline__ BinPick pick_bin256(const uint32_t* h, uint32_t need)
   return {bin, run, cnt};
 }
 
-// Rows of up to kTopkThreads * R columns: the row is read once, into
-// registers (thread t holds columns 4t .. 4t+3 of every 4096-column tile, so
-// the loads coalesce), and the selection works from there.
-//   * Prefilter (rows longer than topk, topk up to half the list): a
-//     threshold T is taken from a sample of the row's keys (kSamples per
-//     thread, spread over the tiles), at the sample's r-th largest key with r
-//     set so that the row holds at least topk keys >= T by a margin of three
-//     standard deviations of the sampling and well under the list's capacity.
-//     A wave counts its keys >= T (and its candidates), reserves that many
-//     slots of an LDS list with one atomic and appends the keys with their
-//     columns (ballot offsets); the radix levels then run over that list
-//     only, over the bits in which T and the row's largest key differ (8 bits
-//     a level, each wave scanning the histogram itself), and the selection is
-//     marked in LDS bitmaps over the columns from the list.  A row with at
-//     most topk candidates takes them all.  If the row holds fewer than topk
-//     keys >= T, or the list overflows, the full selection below runs
-//     instead: the result is the same, only slower.
-//   * Full selection: the first level histograms every key (11 bits), the keys
-//     in its bin are gathered into LDS and the finer levels histogram that
-//     short list; the selection is marked in the bitmaps from the registers.
-//   * The bitmaps give column order directly: a block scan over 32-column
-//     words places each word's columns.
+// ---- the prefilter of the register kernels ----------------------------------
+// A threshold T is taken from a sample of the row's keys (kSamples per
+// thread, from tiles spread over the row), at the sample's r-th largest key
+// with r set so that the row holds at least topk keys >= T by a margin of
+// three standard deviations of the sampling and well under the list's
+// capacity.  A wave counts its keys >= T (and its candidates), reserves that
+// many slots of an LDS list with one atomic and appends the keys with their
+// columns (ballot offsets); the radix levels then run over that list only,
+// over the bits in which T and the row's largest key differ (8 bits a level,
+// each wave scanning the histogram itself), and the selection is marked in
+// LDS bitmaps over the columns from the list.  A row with at most topk
+// candidates takes them all.  If the row holds fewer than topk keys >= T, or
+// the list overflows, a full selection runs instead: the result is the same,
+// only slower.
+
+// The prefilter's per-wave figures.
+struct PrefilterLds {
+  uint32_t smp[3][kTopkWaves];   // sample minimum, maximum, in-range | valid << 16
+  uint32_t list[2][kTopkWaves];  // candidates; largest bits (signed order, biased)
+  uint32_t count;                // list slots reserved
+};
+
+// The threshold T: the lower edge of the sample's bin that holds its rank-r
+// key; 0 when the sample holds no candidate.  smp[q] is the key of the
+// thread's sampled column scol[q] (kKeyNegInf past the range).
+// sh.hist[0, 1024) must be zero; every thread calls it.
+template <int kSamples, int kCap>
+__device__ __forceinline__ uint32_t prefilter_threshold(const uint32_t (&smp)[kSamples],
+                                                        const int (&scol)[kSamples], int n,
+                                                        int topk, TopkShared& sh,
+                                                        PrefilterLds& pf) {
+  const int t = threadIdx.x, lane = t & (kWaveLanes - 1), wave = t >> 6;
+  uint32_t vmin = ~0u, vmax = 0, n_in = 0, n_val = 0;
+#pragma unroll
+  for (int q = 0; q < kSamples; ++q) {
+    const uint32_t v = smp[q];
+    const bool valid = v != kKeyNegInf;       // columns past the range hold -inf keys
+    vmin = valid ? min(vmin, v) : vmin;
+    vmax = valid ? max(vmax, v) : vmax;
+    n_in += __popcll(__ballot(scol[q] < n));
+    n_val += __popcll(__ballot(valid));
+  }
+  vmin = wave_min_u32(vmin);
+  vmax = wave_max_u32(vmax);
+  if (lane == 0) {
+    pf.smp[0][wave] = vmin;
+    pf.smp[1][wave] = vmax;
+    pf.smp[2][wave] = n_in | n_val << 16;
+  }
+  __syncthreads();
+  const bool wl = lane < kTopkWaves;
+  const uint32_t mn = wave_min_u32(wl ? pf.smp[0][lane] : ~0u);
+  const uint32_t mx = wave_max_u32(wl ? pf.smp[1][lane] : 0u);
+  const uint32_t packed = wave_sum_u32(wl ? pf.smp[2][lane] : 0u);
+  const uint32_t s_in = packed & 0xffffu, s_val = packed >> 16;
+  if (s_val == 0) return 0u;
+  // A sample key stands for rho row columns; with r sample keys >= T the
+  // row's count of keys >= T is about r * rho, with a standard deviation of
+  // about rho * sqrt(r).  r solves r * rho - 3 rho sqrt(r) = topk; the
+  // refinement stops once at most r_hi sample keys are >= T.
+  const float rho = (float)n / (float)s_in;
+  const float x = 1.5f + sqrtf(2.25f + (float)topk / rho);
+  uint32_t need = min((uint32_t)ceilf(x * x), s_val);
+  const uint32_t r_hi = max(need, (uint32_t)(0.7f * (float)kCap / rho));
+  uint32_t pre = 0, got = s_val, acc = 0;
+  int pos = 32 - __clz(mx - mn);              // offset bits below the common prefix
+  for (int lvl = 0; pos > 0 && got > r_hi; ++lvl) {
+    const int shf = max(pos - 8, 0);
+    uint32_t* h = sh.hist + 256 * lvl;
+    const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
+#pragma unroll
+    for (int q = 0; q < kSamples; ++q) {
+      const uint32_t off = smp[q] - mn;
+      if (smp[q] != kKeyNegInf && ((off ^ pre) & fixed) == 0)
+        atomicAdd(&h[(off >> shf) & 255u], 1u);
+    }
+    __syncthreads();
+    const BinPick b = pick_bin256(h, need);
+    need -= b.above;
+    acc += b.above;
+    got = acc + b.count;                      // sample keys >= the bin's lower edge
+    pre |= b.bin << shf;
+    pos = shf;
+  }
+  return mn + pre;
+}
+
+// Appends the keys >= T of kT register-held tiles (tiles tile0 ..
+// tile0 + kT - 1 of the row, as fp32 bit patterns with -inf past the range)
+// to the list with their columns, and adds the tiles' candidates to wcand
+// and their largest bits to lmax.  The compares run on the bit patterns: for
+// T at or above +0 (kPos), key >= T exactly when the bits as a signed integer
+// reach T's; for T below -0, exactly when the bits as an unsigned integer are
+// at most T's (every non-negative value, and the negative ones nearer zero).
+// Without t_ok (T not above -inf) nothing is listed.
+template <bool kPos, int kT, int kCap>
+__device__ __forceinline__ void count_and_list(const uint32_t (&k)[kT][4], int tile0, uint32_t T,
+                                               bool t_ok, uint32_t& wcand, int32_t& lmax,
+                                               PrefilterLds& pf, uint2* list_kc) {
+  constexpr int kTile = 4 * kTopkThreads;
+  const int t = threadIdx.x, lane = t & (kWaveLanes - 1);
+  const uint32_t tb = kPos ? T ^ 0x80000000u : ~T;
+  auto passes = [](uint32_t bits, uint32_t thr) {
+    return kPos ? (int32_t)bits >= (int32_t)thr : bits <= thr;
+  };
+  uint32_t wcnt = 0, cand = 0;
+#pragma unroll
+  for (int m = 0; m < kT; ++m)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lmax = max(lmax, (int32_t)k[m][u]);
+      wcnt += __popcll(__ballot(passes(k[m][u], tb)));
+      cand += __popcll(__ballot(k[m][u] != kBitsNegInf));
+    }
+  // the counts are formed here, not where they are used (their masks would
+  // stay live through the writes)
+  asm volatile("" : "+s"(wcnt), "+s"(cand));
+  wcand += cand;
+  uint32_t base = 0;
+  if (t_ok && lane == 0) base = atomicAdd(&pf.count, wcnt);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+  if (t_ok && base + wcnt <= (uint32_t)kCap) {
+    // The compares are made again here: kept from the counting pass, their
+    // masks (two scalar registers per key) would not fit.
+    uint32_t tb2 = tb;
+    asm volatile("" : "+s"(tb2));
+    // the columns are formed again here too (kept from the range checks of
+    // the loads, one per key would stay live)
+    uint32_t col4 = 4 * t + tile0 * kTile;
+    asm volatile("" : "+v"(col4));
+    uint32_t run = base;
+#pragma unroll
+    for (int m = 0; m < kT; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool pass = passes(k[m][u], tb2);
+        const uint64_t b = __ballot(pass);
+        if (pass) {
+          const uint32_t off =
+              run + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+          // a copy made here: paired with its column for the 8-byte store,
+          // the key itself would take a register pair for its whole life
+          uint32_t kv = k[m][u];
+          asm volatile("" : "+v"(kv));
+          list_kc[off] = make_uint2(kv, col4 + (uint32_t)(m * kTile + u));
+        }
+        run += __popcll(b);
+      }
+  }
+}
+
+// After every wave's count_and_list: publishes the wave's candidates and
+// largest bits, waits for the block, and returns the list's length; n_cand
+// receives the row's candidates and U a key at or above every listed key
+// (the largest non-negative value's, or -0's when every value is negative).
+__device__ __forceinline__ uint32_t list_totals(uint32_t wcand, int32_t lmax, PrefilterLds& pf,
+                                                uint32_t& n_cand, uint32_t& U) {
+  const int lane = threadIdx.x & (kWaveLanes - 1), wave = threadIdx.x >> 6;
+  const uint32_t wmax = wave_max_u32((uint32_t)lmax ^ 0x80000000u);   // signed order
+  if (lane == 0) {
+    pf.list[0][wave] = wcand;
+    pf.list[1][wave] = wmax;
+  }
+  __syncthreads();
+  const bool wl = lane < kTopkWaves;
+  n_cand = wave_sum_u32(wl ? pf.list[0][lane] : 0u);
+  const int32_t max_bits = (int32_t)(wave_max_u32(wl ? pf.list[1][lane] : 0u) ^ 0x80000000u);
+  U = max_bits >= 0 ? (uint32_t)max_bits | 0x80000000u : 0x7FFFFFFFu;
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)pf.count);
+}
+
+// The selection from a complete list of `total` (>= topk) keys >= T, all at
+// most U: radix levels over the bits where T and U differ (histograms in
+// sh.hist[1024, 2048), zero), then the marks of the listed columns in gmap
+// (key > K) and qmap (key == K).  Every thread calls it.
+__device__ __forceinline__ void list_select_mark(uint32_t total, uint32_t T, uint32_t U, int topk,
+                                                 TopkShared& sh, const uint2* list_kc,
+                                                 uint32_t* gmap, uint32_t* qmap, uint32_t& K,
+                                                 uint32_t& need_eq) {
+  const int t = threadIdx.x;
+  uint32_t need = (uint32_t)topk;
+  int pos = 32 - __clz(U ^ T);
+  uint32_t prefix = pos >= 32 ? 0u : U & (~0u << pos);
+  bool whole = false;
+  for (int lvl = 0; pos > 0; ++lvl) {
+    const int shf = max(pos - 8, 0);
+    uint32_t* h = sh.hist + 1024 + 256 * lvl;
+    const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
+    for (int i = t; i < (int)total; i += kTopkThreads) {
+      const uint32_t key = order_key(list_kc[i].x);
+      if (((key ^ prefix) & fixed) == 0) atomicAdd(&h[(key >> shf) & 255u], 1u);
+    }
+    __syncthreads();
+    const BinPick b = pick_bin256(h, need);
+    need -= b.above;
+    prefix |= b.bin << shf;
+    pos = shf;
+    if (pos > 0 && b.count == need && prefix != 0) {   // the whole bin is taken
+      whole = true;
+      break;
+    }
+  }
+  K = whole ? prefix - 1u : prefix;
+  need_eq = whole ? 0u : need;
+  for (int i = t; i < (int)total; i += kTopkThreads) {
+    const uint2 e = list_kc[i];
+    const uint32_t key = order_key(e.x);
+    const int c = (int)e.y;
+    if (key > K) atomicOr(&gmap[c >> 5], 1u << (c & 31));
+    else if (key == K) atomicOr(&qmap[c >> 5], 1u << (c & 31));
+  }
+}
+
+// ---- ordered write ---------------------------------------------------------
+// The block walks the bitmaps gmap (key > K) and qmap (key == K) one
+// 32-column word at a time in column order: a scan of the words' counts
+// gives each word's first output slot and how many of its == K columns are
+// still taken (the first need_eq in column order); each word's columns are
+// written in ascending order (column s + the word's bit), then -1 up to topk.
+// Every thread calls it, after the bitmaps are complete.
+template <int kWords>
+__device__ __forceinline__ void ordered_write(const uint32_t* gmap, const uint32_t* qmap,
+                                              uint32_t need_eq, int topk, int s, int32_t* out,
+                                              TopkShared& sh) {
+  const int t = threadIdx.x;
+  constexpr int kWpt = (kWords + kTopkThreads - 1) / kTopkThreads;   // per thread
+  uint32_t wg[kWpt], wq[kWpt];
+  uint32_t cg = 0, cq = 0;
+#pragma unroll
+  for (int j = 0; j < kWpt; ++j) {
+    const int w = t * kWpt + j;
+    wg[j] = w < kWords ? gmap[w] : 0u;
+    wq[j] = w < kWords ? qmap[w] : 0u;
+    cg += __popc(wg[j]);
+    cq += __popc(wq[j]);
+  }
+  uint64_t total;
+  const uint64_t before =
+      block_exclusive_scan<uint64_t>(((uint64_t)cq << 32) | cg, sh.wave_sums64, &total);
+  uint32_t gb = (uint32_t)before, qb = (uint32_t)(before >> 32);
+  // columns written: all keys > K, then need_eq of the == K ones (topk, or
+  // every candidate when all are taken)
+  const uint32_t n_sel =
+      min((uint32_t)topk, (uint32_t)total + min(need_eq, (uint32_t)(total >> 32)));
+#pragma unroll
+  for (int j = 0; j < kWpt; ++j) {
+    // the == K columns of this word still taken: the lowest `take` set bits
+    // the == K columns placed before this word, and how many of this word's
+    // are taken.  Written without a guarded subtraction: as
+    // `qb < need_eq ? min(need_eq - qb, nq) : 0`, LLVM evaluated the
+    // subtraction unconditionally with its no-wrap flag and then folded
+    // min(qb, need_eq) below to qb, a wrong position when qb > need_eq.
+    const uint32_t nq = __popc(wq[j]);
+    const uint32_t placed = min(qb, need_eq);
+    uint32_t take = min(need_eq - placed, nq);
+    uint32_t sel_q = 0, rest = wq[j];
+    for (; take > 0; --take) {
+      const uint32_t low = rest & (0u - rest);
+      sel_q |= low;
+      rest ^= low;
+    }
+    uint32_t word = wg[j] | sel_q;
+    uint32_t pos = gb + placed;
+    const int col0 = s + 32 * (t * kWpt + j);
+    while (word) {
+      const int b = __builtin_ctz(word);
+      word &= word - 1;
+      if (pos < (uint32_t)topk) out[pos] = col0 + b;
+      ++pos;
+    }
+    gb += __popc(wg[j]);
+    qb += nq;
+  }
+  for (int pos = (int)n_sel + t; pos < topk; pos += kTopkThreads) out[pos] = -1;
+}
+
+// Rows of up to kTopkThreads * R columns (R up to 32): the row is read once,
+// into registers (thread t holds columns 4t .. 4t+3 of every 4096-column
+// tile, so the loads coalesce), and the selection works from there: the
+// prefilter above (rows longer than topk, topk up to half the list), else a
+// full selection: the first level histograms every key (11 bits), the keys
+// in its bin are gathered into LDS and the finer levels histogram that short
+// list; the selection is marked in the bitmaps from the registers.  The
+// bitmaps give column order directly (ordered_write).
 // Up to 32 keys per thread: at most 64 VGPRs, so two blocks (8 waves per
 // SIMD) share a compute unit and one block's loads overlap the other's work.
 template <int IN, int R>
-__global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel(TopkParams p) {
-  static_assert(R % 4 == 0 && R <= 64, "whole 4-column groups; the flag words hold 64");
+__global__ __launch_bounds__(kTopkThreads, 8) void topk_reg_kernel(TopkParams p) {
+  static_assert(R % 4 == 0 && R <= 32, "whole 4-column groups; 64 VGPRs");
   constexpr int kTiles = R / 4;
   constexpr int kTile = 4 * kTopkThreads;
   constexpr int kWords = kTiles * kTile / 32;  // 32-column words of the register-held row
-  constexpr int kCap = R > 32 ? 8192 : 5120;   // LDS list: prefilter keys, or one bin's keys
-  constexpr int kSamples = R >= 32 ? R / 16 : 1;
+  constexpr int kCap = 5120;                   // LDS list: prefilter keys, or one bin's keys
+  constexpr int kSamples = R >= 32 ? R / 16 : 1;   // sample keys per thread
   static_assert((kTiles & (kTiles - 1)) == 0 && kTiles % kSamples == 0, "sample tiles");
   __shared__ TopkShared sh;
   __shared__ union {
@@ -496,13 +765,10 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   uint32_t* const qmap = u_.maps + kWords;
   __shared__ uint2 list_kc[kCap];             // the prefilter's (bit pattern, column) pairs
   uint32_t* const bin_keys = reinterpret_cast<uint32_t*>(list_kc);   // or the first-level bin's keys
-  __shared__ uint32_t smp_stat[3][kTopkWaves];
-  __shared__ uint32_t list_stat[2][kTopkWaves];
-  __shared__ uint32_t list_count;
+  __shared__ PrefilterLds pf;
   __shared__ uint32_t bin_count;
   const int t = threadIdx.x;
   const int lane = t & (kWaveLanes - 1);
-  const int wave = t >> 6;
   const int64_t row = blockIdx.x;
   int s = 0, e = p.skv;
   if (p.k_start) {
@@ -531,186 +797,31 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   if (!take_all && p.topk <= kCap / 2) {
     for (int b = t; b < 2048; b += kTopkThreads) sh.hist[b] = 0;
     for (int w = t; w < 2 * kWords; w += kTopkThreads) u_.maps[w] = 0;
-    if (t == 0) list_count = 0;
-    // ---- the sample: kSamples keys per thread, tiles spread over the row ----
+    if (t == 0) pf.count = 0;
+    // the sample, from the registers: thread t's first column of tile
+    // (t + q kTiles / kSamples) mod kTiles
     uint32_t smp[kSamples];
-    uint32_t vmin = ~0u, vmax = 0, n_in = 0, n_val = 0;
+    int scol[kSamples];
 #pragma unroll
     for (int q = 0; q < kSamples; ++q) {
       const int tq = (t + q * (kTiles / kSamples)) & (kTiles - 1);
       uint32_t v = k[0][0];
 #pragma unroll
       for (int m = 1; m < kTiles; ++m) v = tq == m ? k[m][0] : v;
-      v = order_key(v);
-      smp[q] = v;
-      const bool valid = v != kKeyNegInf;     // columns past the range hold -inf keys
-      vmin = valid ? min(vmin, v) : vmin;
-      vmax = valid ? max(vmax, v) : vmax;
-      n_in += __popcll(__ballot(tq * kTile + 4 * t < n));
-      n_val += __popcll(__ballot(valid));
+      smp[q] = order_key(v);
+      scol[q] = tq * kTile + 4 * t;
     }
-    vmin = wave_min_u32(vmin);
-    vmax = wave_max_u32(vmax);
-    if (lane == 0) {
-      smp_stat[0][wave] = vmin;
-      smp_stat[1][wave] = vmax;
-      smp_stat[2][wave] = n_in | n_val << 16;
-    }
-    __syncthreads();
-    const bool wl = lane < kTopkWaves;
-    const uint32_t mn = wave_min_u32(wl ? smp_stat[0][lane] : ~0u);
-    const uint32_t mx = wave_max_u32(wl ? smp_stat[1][lane] : 0u);
-    const uint32_t packed = wave_sum_u32(wl ? smp_stat[2][lane] : 0u);
-    const uint32_t s_in = packed & 0xffffu, s_val = packed >> 16;
-
-    // ---- the threshold: the lower edge of the sample's bin holding rank r ----
-    // A sample key stands for rho row columns; with r sample keys >= T the
-    // row's count of keys >= T is about r * rho, with a standard deviation of
-    // about rho * sqrt(r).  r solves r * rho - 3 rho sqrt(r) = topk; the
-    // refinement stops once at most r_hi sample keys are >= T.
-    uint32_t T = 0;
-    if (s_val > 0) {
-      const float rho = (float)n / (float)s_in;
-      const float x = 1.5f + sqrtf(2.25f + (float)p.topk / rho);
-      uint32_t need = min((uint32_t)ceilf(x * x), s_val);
-      const uint32_t r_hi = max(need, (uint32_t)(0.7f * (float)kCap / rho));
-      uint32_t pre = 0, got = s_val, acc = 0;
-      int pos = 32 - __clz(mx - mn);          // offset bits below the common prefix
-      for (int lvl = 0; pos > 0 && got > r_hi; ++lvl) {
-        const int shf = max(pos - 8, 0);
-        uint32_t* h = sh.hist + 256 * lvl;
-        const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
-#pragma unroll
-        for (int q = 0; q < kSamples; ++q) {
-          const uint32_t off = smp[q] - mn;
-          if (smp[q] != kKeyNegInf && ((off ^ pre) & fixed) == 0)
-            atomicAdd(&h[(off >> shf) & 255u], 1u);
-        }
-        __syncthreads();
-        const BinPick b = pick_bin256(h, need);
-        need -= b.above;
-        acc += b.above;
-        got = acc + b.count;                  // sample keys >= the bin's lower edge
-        pre |= b.bin << shf;
-        pos = shf;
-      }
-      T = mn + pre;
-    }
-
-    // ---- the list: every key >= T with its column, the row's candidates and
-    // its largest key.  A wave counts its keys >= T, reserves their slots with
-    // one LDS atomic and writes them (ballot offsets); a wave whose keys do not
-    // fit writes none (the list then overflows and the full selection runs).
-    // The compares run on the raw bit patterns: for T at or above +0, key >= T
-    // exactly when the bits as a signed integer reach T's; for T below -0,
-    // exactly when the bits as an unsigned integer are at most T's (every
-    // non-negative value, and the negative ones nearer zero).  The row's
-    // largest key is bounded by its largest bits as a signed integer (its
-    // largest non-negative value), or by -0 when every value is negative.
+    const uint32_t T = prefilter_threshold<kSamples, kCap>(smp, scol, n, p.topk, sh, pf);
     const bool t_ok = T > kKeyNegInf;
-    const bool t_pos = T >= 0x80000000u;
-    uint32_t wcnt = 0, wcand = 0;
+    uint32_t wcand = 0;
     int32_t lmax = INT32_MIN;
-    auto count_and_list = [&](auto pos_tag) {
-      constexpr bool kPos = decltype(pos_tag)::value;
-      const uint32_t tb = kPos ? T ^ 0x80000000u : ~T;
-      auto passes = [](uint32_t bits, uint32_t thr) {
-        return kPos ? (int32_t)bits >= (int32_t)thr : bits <= thr;
-      };
-#pragma unroll
-      for (int m = 0; m < kTiles; ++m)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          lmax = max(lmax, (int32_t)k[m][u]);
-          wcnt += __popcll(__ballot(passes(k[m][u], tb)));
-          wcand += __popcll(__ballot(k[m][u] != kBitsNegInf));
-        }
-      // the counts are formed here, not where they are used (their 32 masks
-      // would stay live through the writes)
-      asm volatile("" : "+s"(wcnt), "+s"(wcand));
-      uint32_t base = 0;
-      if (t_ok && lane == 0) base = atomicAdd(&list_count, wcnt);
-      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-      if (t_ok && base + wcnt <= (uint32_t)kCap) {
-        // The compares are made again here: kept from the counting pass, their
-        // masks (two scalar registers per key) would not fit.
-        uint32_t tb2 = tb;
-        asm volatile("" : "+s"(tb2));
-        // the columns are formed again here too (kept from the range checks
-        // of the loads, 32 of them would stay live)
-        uint32_t col4 = 4 * t;
-        asm volatile("" : "+v"(col4));
-        uint32_t run = base;
-#pragma unroll
-        for (int m = 0; m < kTiles; ++m)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool pass = passes(k[m][u], tb2);
-            const uint64_t b = __ballot(pass);
-            if (pass) {
-              const uint32_t off =
-                  run + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-              // a copy made here: paired with its column for the 8-byte
-              // store, the key itself would take a register pair for its
-              // whole life
-              uint32_t kv = k[m][u];
-              asm volatile("" : "+v"(kv));
-              list_kc[off] = make_uint2(kv, col4 + (uint32_t)(m * kTile + u));
-            }
-            run += __popcll(b);
-          }
-      }
-    };
-    if (t_pos) count_and_list(std::true_type{});
-    else count_and_list(std::false_type{});
-    const uint32_t wmax = wave_max_u32((uint32_t)lmax ^ 0x80000000u);   // signed order
-    if (lane == 0) {
-      list_stat[0][wave] = wcand;
-      list_stat[1][wave] = wmax;
-    }
-    __syncthreads();
-    const uint32_t total = (uint32_t)__builtin_amdgcn_readfirstlane((int)list_count);
-    const uint32_t n_cand = wave_sum_u32(wl ? list_stat[0][lane] : 0u);
-    const int32_t max_bits = (int32_t)(wave_max_u32(wl ? list_stat[1][lane] : 0u) ^ 0x80000000u);
-    const uint32_t U = max_bits >= 0 ? (uint32_t)max_bits | 0x80000000u : 0x7FFFFFFFu;
+    if (T >= 0x80000000u) count_and_list<true, kTiles, kCap>(k, 0, T, t_ok, wcand, lmax, pf, list_kc);
+    else count_and_list<false, kTiles, kCap>(k, 0, T, t_ok, wcand, lmax, pf, list_kc);
+    uint32_t n_cand, U;
+    const uint32_t total = list_totals(wcand, lmax, pf, n_cand, U);
     take_all = n_cand <= (uint32_t)p.topk;
     fast = !take_all && t_ok && total >= (uint32_t)p.topk && total <= (uint32_t)kCap;
-
-    if (fast) {
-      // ---- radix levels over the list, on the bits where T and U differ ----
-      uint32_t need = (uint32_t)p.topk;
-      int pos = 32 - __clz(U ^ T);
-      uint32_t prefix = pos >= 32 ? 0u : U & (~0u << pos);
-      bool whole = false;
-      for (int lvl = 0; pos > 0; ++lvl) {
-        const int shf = max(pos - 8, 0);
-        uint32_t* h = sh.hist + 1024 + 256 * lvl;
-        const uint32_t fixed = pos >= 32 ? 0u : ~0u << pos;
-        for (int i = t; i < (int)total; i += kTopkThreads) {
-          const uint32_t key = order_key(list_kc[i].x);
-          if (((key ^ prefix) & fixed) == 0) atomicAdd(&h[(key >> shf) & 255u], 1u);
-        }
-        __syncthreads();
-        const BinPick b = pick_bin256(h, need);
-        need -= b.above;
-        prefix |= b.bin << shf;
-        pos = shf;
-        if (pos > 0 && b.count == need && prefix != 0) {   // the whole bin is taken
-          whole = true;
-          break;
-        }
-      }
-      K = whole ? prefix - 1u : prefix;
-      need_eq = whole ? 0u : need;
-      for (int i = t; i < (int)total; i += kTopkThreads) {
-        const uint2 e = list_kc[i];
-        const uint32_t key = order_key(e.x);
-        const int c = (int)e.y;
-        if (key > K) atomicOr(&gmap[c >> 5], 1u << (c & 31));
-        else if (key == K) atomicOr(&qmap[c >> 5], 1u << (c & 31));
-      }
-    }
+    if (fast) list_select_mark(total, T, U, p.topk, sh, list_kc, gmap, qmap, K, need_eq);
   }
 
   if (!fast) {
@@ -827,61 +938,91 @@ __global__ __launch_bounds__(kTopkThreads, R <= 32 ? 8 : 4) void topk_reg_kernel
   }
   __syncthreads();
 
-  // ---- ordered write ---------------------------------------------------------
-  // The block walks the bitmaps gmap (key > K) and qmap (key == K) one
-  // 32-column word at a time in column order: a scan of the words' counts
-  // gives each word's first output slot and how many of its == K columns are
-  // still taken (the first need_eq in column order); each word's columns are
-  // written in ascending order.
-  constexpr int kWpt = (kWords + kTopkThreads - 1) / kTopkThreads;   // per thread
-  uint32_t wg[kWpt], wq[kWpt];
-  uint32_t cg = 0, cq = 0;
-#pragma unroll
-  for (int j = 0; j < kWpt; ++j) {
-    const int w = t * kWpt + j;
-    wg[j] = w < kWords ? gmap[w] : 0u;
-    wq[j] = w < kWords ? qmap[w] : 0u;
-    cg += __popc(wg[j]);
-    cq += __popc(wq[j]);
+  ordered_write<kWords>(gmap, qmap, need_eq, p.topk, s, out, sh);
+}
+
+// Rows of 32769 .. 65536 columns: the register kernel's prefilter with the
+// row loaded in two halves of 32 keys per thread (each counted and listed in
+// turn), so the block stays within 64 VGPRs and two blocks share a compute
+// unit; the sample is loaded apart, before the row.  A row the prefilter
+// does not settle (at most topk candidates, topk above half the list, too
+// few keys >= T, a full list) is read again by the streaming selection.
+template <int IN>
+__global__ __launch_bounds__(kTopkThreads, 8) void topk_half_kernel(TopkParams p) {
+  constexpr int kTiles = 16, kHalf = 8;
+  constexpr int kTile = 4 * kTopkThreads;
+  constexpr int kWords = kTiles * kTile / 32;
+  constexpr int kCap = 6144;
+  constexpr int kSamples = 4;
+  __shared__ TopkShared sh;
+  __shared__ union {
+    struct {
+      uint32_t maps[2 * kWords];              // the column bitmaps (key > K, key == K)
+      uint2 list_kc[kCap];                    // the prefilter's (bit pattern, column) pairs
+    } f;
+    TopkLists ls;                             // the streaming selection's lists
+  } u_;
+  __shared__ PrefilterLds pf;
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  int s = 0, e = p.skv;
+  if (p.k_start) {
+    s = clampi(p.k_start[row], 0, p.skv);
+    e = clampi(p.k_end[row], s, p.skv);
   }
-  uint64_t total;
-  const uint64_t before =
-      block_exclusive_scan<uint64_t>(((uint64_t)cq << 32) | cg, sh.wave_sums64, &total);
-  uint32_t gb = (uint32_t)before, qb = (uint32_t)(before >> 32);
-  // columns written: all keys > K, then need_eq of the == K ones (topk, or
-  // every candidate when all are taken)
-  const uint32_t n_sel =
-      min((uint32_t)p.topk, (uint32_t)total + min(need_eq, (uint32_t)(total >> 32)));
-#pragma unroll
-  for (int j = 0; j < kWpt; ++j) {
-    // the == K columns of this word still taken: the lowest `take` set bits
-    // the == K columns placed before this word, and how many of this word's
-    // are taken.  Written without a guarded subtraction: as
-    // `qb < need_eq ? min(need_eq - qb, nq) : 0`, LLVM evaluated the
-    // subtraction unconditionally with its no-wrap flag and then folded
-    // min(qb, need_eq) below to qb, a wrong position when qb > need_eq.
-    const uint32_t nq = __popc(wq[j]);
-    const uint32_t placed = min(qb, need_eq);
-    uint32_t take = min(need_eq - placed, nq);
-    uint32_t sel_q = 0, rest = wq[j];
-    for (; take > 0; --take) {
-      const uint32_t low = rest & (0u - rest);
-      sel_q |= low;
-      rest ^= low;
-    }
-    uint32_t word = wg[j] | sel_q;
-    uint32_t pos = gb + placed;
-    const int col0 = s + 32 * (t * kWpt + j);
-    while (word) {
-      const int b = __builtin_ctz(word);
-      word &= word - 1;
-      if (pos < (uint32_t)p.topk) out[pos] = col0 + b;
-      ++pos;
-    }
-    gb += __popc(wg[j]);
-    qb += nq;
+  const int n = e - s;
+  if (n <= p.topk || p.topk > kCap / 2) {
+    topk_stream_row<IN>(p, row, sh, u_.ls);
+    return;
   }
-  for (int pos = (int)n_sel + t; pos < p.topk; pos += kTopkThreads) out[pos] = -1;
+  constexpr int kIB = IN == kBF16 ? 2 : 4;
+  const TopkRow<IN> src{make_rsrc(static_cast<const char*>(p.logits) + row * p.stride * kIB,
+                                  (uint32_t)(p.skv * kIB)),
+                        s, p.skv - 1 - s};
+  int32_t* out = p.indices + row * p.out_stride;
+
+  // the sample, loaded: thread t's first column of tile (wave + q kTiles /
+  // kSamples) mod kTiles (one tile per wave and load, so a wave's loads fall
+  // on adjacent lines)
+  uint32_t smp[kSamples];
+  int scol[kSamples];
+  const int wave = t >> 6;
+#pragma unroll
+  for (int q = 0; q < kSamples; ++q) {
+    scol[q] = ((wave + q * (kTiles / kSamples)) & (kTiles - 1)) * kTile + 4 * t;
+    smp[q] = scol[q] < n ? src.key(scol[q]) : kKeyNegInf;
+  }
+  for (int b = t; b < 2048; b += kTopkThreads) sh.hist[b] = 0;
+  for (int w = t; w < 2 * kWords; w += kTopkThreads) u_.f.maps[w] = 0;
+  if (t == 0) pf.count = 0;
+  const uint32_t T = prefilter_threshold<kSamples, kCap>(smp, scol, n, p.topk, sh, pf);
+  const bool t_ok = T > kKeyNegInf;
+  uint32_t wcand = 0;
+  int32_t lmax = INT32_MIN;
+#pragma nounroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t k[kHalf][4];
+#pragma unroll
+    for (int m = 0; m < kHalf; ++m) {
+      const int tile = h * kHalf + m;
+      src.bits4(tile * kTile + 4 * t, n, (tile + 1) * kTile <= n, k[m]);
+    }
+    if (T >= 0x80000000u) count_and_list<true, kHalf, kCap>(k, h * kHalf, T, t_ok, wcand, lmax, pf, u_.f.list_kc);
+    else count_and_list<false, kHalf, kCap>(k, h * kHalf, T, t_ok, wcand, lmax, pf, u_.f.list_kc);
+  }
+  uint32_t n_cand, U;
+  const uint32_t total = list_totals(wcand, lmax, pf, n_cand, U);
+  if (n_cand <= (uint32_t)p.topk || !t_ok || total < (uint32_t)p.topk ||
+      total > (uint32_t)kCap) {
+    __syncthreads();                          // the lists reuse the prefilter's LDS
+    topk_stream_row<IN>(p, row, sh, u_.ls);
+    return;
+  }
+  uint32_t K, need_eq;
+  list_select_mark(total, T, U, p.topk, sh, u_.f.list_kc, u_.f.maps, u_.f.maps + kWords, K,
+                   need_eq);
+  __syncthreads();
+  ordered_write<kWords>(u_.f.maps, u_.f.maps + kWords, need_eq, p.topk, s, out, sh);
 }
 
 template <int IN>
@@ -894,7 +1035,7 @@ static hipError_t launch_topk_in(const TopkParams& p, hipStream_t s) {
   } else if (p.skv <= 32 * kTopkThreads) {
     hipLaunchKernelGGL((topk_reg_kernel<IN, 32>), grid, block, 0, s, p);
   } else if (p.skv <= 64 * kTopkThreads) {
-    hipLaunchKernelGGL((topk_reg_kernel<IN, 64>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((topk_half_kernel<IN>), grid, block, 0, s, p);
   } else {
     hipLaunchKernelGGL((topk_stream_kernel<IN>), grid, block, 0, s, p);
   }
