@@ -477,7 +477,7 @@ __device__ __forceinline__ BinPick pick_bin256(const uint32_t* h, uint32_t need)
 // The prefilter's per-wave figures.
 struct PrefilterLds {
   uint32_t smp[3][kTopkWaves];   // sample minimum, maximum, in-range | valid << 16
-  uint32_t list[2][kTopkWaves];  // candidates; largest bits (signed order, biased)
+  uint32_t list[2][kTopkWaves];  // candidates (counted when needed); largest bits (biased)
   uint32_t count;                // list slots reserved
 };
 
@@ -548,35 +548,32 @@ __device__ __forceinline__ uint32_t prefilter_threshold(const uint32_t (&smp)[kS
 
 // Appends the keys >= T of kT register-held tiles (tiles tile0 ..
 // tile0 + kT - 1 of the row, as fp32 bit patterns with -inf past the range)
-// to the list with their columns, and adds the tiles' candidates to wcand
-// and their largest bits to lmax.  The compares run on the bit patterns: for
+// to the list with their columns, and folds their largest bits into lmax.  The compares run on the bit patterns: for
 // T at or above +0 (kPos), key >= T exactly when the bits as a signed integer
 // reach T's; for T below -0, exactly when the bits as an unsigned integer are
 // at most T's (every non-negative value, and the negative ones nearer zero).
 // Without t_ok (T not above -inf) nothing is listed.
 template <bool kPos, int kT, int kCap>
 __device__ __forceinline__ void count_and_list(const uint32_t (&k)[kT][4], int tile0, uint32_t T,
-                                               bool t_ok, uint32_t& wcand, int32_t& lmax,
-                                               PrefilterLds& pf, uint2* list_kc) {
+                                               bool t_ok, int32_t& lmax, PrefilterLds& pf,
+                                               uint2* list_kc) {
   constexpr int kTile = 4 * kTopkThreads;
   const int t = threadIdx.x, lane = t & (kWaveLanes - 1);
   const uint32_t tb = kPos ? T ^ 0x80000000u : ~T;
   auto passes = [](uint32_t bits, uint32_t thr) {
     return kPos ? (int32_t)bits >= (int32_t)thr : bits <= thr;
   };
-  uint32_t wcnt = 0, cand = 0;
+  uint32_t wcnt = 0;
 #pragma unroll
   for (int m = 0; m < kT; ++m)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       lmax = max(lmax, (int32_t)k[m][u]);
       wcnt += __popcll(__ballot(passes(k[m][u], tb)));
-      cand += __popcll(__ballot(k[m][u] != kBitsNegInf));
     }
-  // the counts are formed here, not where they are used (their masks would
-  // stay live through the writes)
-  asm volatile("" : "+s"(wcnt), "+s"(cand));
-  wcand += cand;
+  // the count is formed here, not where it is used (its masks would stay
+  // live through the writes)
+  asm volatile("" : "+s"(wcnt));
   uint32_t base = 0;
   if (t_ok && lane == 0) base = atomicAdd(&pf.count, wcnt);
   base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
@@ -611,21 +608,16 @@ __device__ __forceinline__ void count_and_list(const uint32_t (&k)[kT][4], int t
   }
 }
 
-// After every wave's count_and_list: publishes the wave's candidates and
-// largest bits, waits for the block, and returns the list's length; n_cand
-// receives the row's candidates and U a key at or above every listed key
-// (the largest non-negative value's, or -0's when every value is negative).
-__device__ __forceinline__ uint32_t list_totals(uint32_t wcand, int32_t lmax, PrefilterLds& pf,
-                                                uint32_t& n_cand, uint32_t& U) {
+// After every wave's count_and_list: publishes the wave's largest bits,
+// waits for the block, and returns the list's length; U receives a key at or
+// above every listed key (the largest non-negative value's, or -0's when
+// every value is negative).
+__device__ __forceinline__ uint32_t list_totals(int32_t lmax, PrefilterLds& pf, uint32_t& U) {
   const int lane = threadIdx.x & (kWaveLanes - 1), wave = threadIdx.x >> 6;
   const uint32_t wmax = wave_max_u32((uint32_t)lmax ^ 0x80000000u);   // signed order
-  if (lane == 0) {
-    pf.list[0][wave] = wcand;
-    pf.list[1][wave] = wmax;
-  }
+  if (lane == 0) pf.list[1][wave] = wmax;
   __syncthreads();
   const bool wl = lane < kTopkWaves;
-  n_cand = wave_sum_u32(wl ? pf.list[0][lane] : 0u);
   const int32_t max_bits = (int32_t)(wave_max_u32(wl ? pf.list[1][lane] : 0u) ^ 0x80000000u);
   U = max_bits >= 0 ? (uint32_t)max_bits | 0x80000000u : 0x7FFFFFFFu;
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)pf.count);
@@ -813,14 +805,23 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_reg_kernel(TopkParams p)
     }
     const uint32_t T = prefilter_threshold<kSamples, kCap>(smp, scol, n, p.topk, sh, pf);
     const bool t_ok = T > kKeyNegInf;
-    uint32_t wcand = 0;
     int32_t lmax = INT32_MIN;
-    if (T >= 0x80000000u) count_and_list<true, kTiles, kCap>(k, 0, T, t_ok, wcand, lmax, pf, list_kc);
-    else count_and_list<false, kTiles, kCap>(k, 0, T, t_ok, wcand, lmax, pf, list_kc);
-    uint32_t n_cand, U;
-    const uint32_t total = list_totals(wcand, lmax, pf, n_cand, U);
-    take_all = n_cand <= (uint32_t)p.topk;
-    fast = !take_all && t_ok && total >= (uint32_t)p.topk && total <= (uint32_t)kCap;
+    if (T >= 0x80000000u) count_and_list<true, kTiles, kCap>(k, 0, T, t_ok, lmax, pf, list_kc);
+    else count_and_list<false, kTiles, kCap>(k, 0, T, t_ok, lmax, pf, list_kc);
+    uint32_t U;
+    const uint32_t total = list_totals(lmax, pf, U);
+    if (total < (uint32_t)p.topk) {           // too few keys >= T: count the candidates
+      uint32_t cand = 0;
+#pragma unroll
+      for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cand += __popcll(__ballot(k[m][u] != kBitsNegInf));
+      if (lane == 0) pf.list[0][t >> 6] = cand;
+      __syncthreads();
+      const uint32_t n_cand = wave_sum_u32(lane < kTopkWaves ? pf.list[0][lane] : 0u);
+      take_all = n_cand <= (uint32_t)p.topk;
+    }
+    fast = t_ok && total >= (uint32_t)p.topk && total <= (uint32_t)kCap;
     if (fast) list_select_mark(total, T, U, p.topk, sh, list_kc, gmap, qmap, K, need_eq);
   }
 
@@ -997,7 +998,6 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_half_kernel(TopkParams p
   if (t == 0) pf.count = 0;
   const uint32_t T = prefilter_threshold<kSamples, kCap>(smp, scol, n, p.topk, sh, pf);
   const bool t_ok = T > kKeyNegInf;
-  uint32_t wcand = 0;
   int32_t lmax = INT32_MIN;
 #pragma nounroll
   for (int h = 0; h < 2; ++h) {
@@ -1007,13 +1007,12 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_half_kernel(TopkParams p
       const int tile = h * kHalf + m;
       src.bits4(tile * kTile + 4 * t, n, (tile + 1) * kTile <= n, k[m]);
     }
-    if (T >= 0x80000000u) count_and_list<true, kHalf, kCap>(k, h * kHalf, T, t_ok, wcand, lmax, pf, u_.f.list_kc);
-    else count_and_list<false, kHalf, kCap>(k, h * kHalf, T, t_ok, wcand, lmax, pf, u_.f.list_kc);
+    if (T >= 0x80000000u) count_and_list<true, kHalf, kCap>(k, h * kHalf, T, t_ok, lmax, pf, u_.f.list_kc);
+    else count_and_list<false, kHalf, kCap>(k, h * kHalf, T, t_ok, lmax, pf, u_.f.list_kc);
   }
-  uint32_t n_cand, U;
-  const uint32_t total = list_totals(wcand, lmax, pf, n_cand, U);
-  if (n_cand <= (uint32_t)p.topk || !t_ok || total < (uint32_t)p.topk ||
-      total > (uint32_t)kCap) {
+  uint32_t U;
+  const uint32_t total = list_totals(lmax, pf, U);
+  if (!t_ok || total < (uint32_t)p.topk || total > (uint32_t)kCap) {
     __syncthreads();                          // the lists reuse the prefilter's LDS
     topk_stream_row<IN>(p, row, sh, u_.ls);
     return;
