@@ -46,7 +46,7 @@ template <int IN>
 struct TopkRow {
   Rsrc r;                                 // the row's Skv elements
   int s;                                  // first column of the range (element offset)
-  int last;                               // the row's last column, relative to s
+  int last;                               // the buffer's last column, relative to s
   // Key of column s + c (c relative to the range start).  The caller keeps
   // c inside the range.
   __device__ __forceinline__ uint32_t key(int c) const {
@@ -70,9 +70,9 @@ struct TopkRow {
       bits[1] = (uint32_t)w[0] & 0xffff0000u;
       bits[2] = (uint32_t)w[1] << 16;
       bits[3] = (uint32_t)w[1] & 0xffff0000u;
-      // The buffer checks each 4-byte half of the load against the row's
-      // end and reads a half that crosses it as zero: when the row's last
-      // column (odd Skv) opens a half, that column is read on its own.
+      // The buffer checks each 4-byte half of the load against its end and
+      // reads a half that crosses it as zero: when the buffer's last column
+      // (an odd end) opens a half, that column is read on its own.
       const int lu = last - c;
       if (lu == 0 || lu == 2)
         bits[lu] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, 2 * (s + c + lu), 0, 0) << 16;
@@ -769,9 +769,12 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_reg_kernel(TopkParams p)
   }
   const int n = e - s;                        // <= kTopkThreads * R (host dispatch)
   constexpr int kIB = IN == kBF16 ? 2 : 4;
+  // The buffer ends with the range: loads past it read zeros without going to
+  // memory (short ranges read only their columns), and the masks below turn
+  // them into -inf.
   const TopkRow<IN> src{make_rsrc(static_cast<const char*>(p.logits) + row * p.stride * kIB,
-                                  (uint32_t)(p.skv * kIB)),
-                        s, p.skv - 1 - s};
+                                  (uint32_t)(e * kIB)),
+                        s, n - 1};
   int32_t* out = p.indices + row * p.out_stride;
 
   // The row's fp32 bit patterns, -inf past the range (only a tile the range
@@ -977,9 +980,10 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_half_kernel(TopkParams p
     return;
   }
   constexpr int kIB = IN == kBF16 ? 2 : 4;
+  // the buffer ends with the range (loads past it read zeros, masked to -inf)
   const TopkRow<IN> src{make_rsrc(static_cast<const char*>(p.logits) + row * p.stride * kIB,
-                                  (uint32_t)(p.skv * kIB)),
-                        s, p.skv - 1 - s};
+                                  (uint32_t)(e * kIB)),
+                        s, n - 1};
   int32_t* out = p.indices + row * p.out_stride;
 
   // the sample, loaded: thread t's first column of tile (wave + q kTiles /
