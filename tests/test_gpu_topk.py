@@ -281,3 +281,34 @@ def test_topk_value_distributions(kind):
         log(f"[topk] {what}")
         got = mq.mqa_logits_topk(t, topk, dev(ks), dev(ke)).cpu().numpy()
         assert np.array_equal(got, oracle.topk_indices(x, topk, ks, ke)), what
+
+
+@pytest.mark.parametrize("skv", [3000, 12000, 40000])
+def test_topk_range_ends_bound_the_reads(skv):
+    # the row's buffer ends with its range: a huge value just past the end is
+    # never a candidate, and the last column in range (odd or even end, bf16
+    # and fp32) is read and taken
+    import mqa_logits_amd as mq
+    rng = np.random.default_rng(skv + 1)
+    sq = 12
+    x = rng.standard_normal((sq, skv)).astype(np.float32)
+    ks = rng.integers(0, skv // 3, sq).astype(np.int32)
+    ke = (ks + rng.integers(skv // 4, skv - skv // 3, sq)).astype(np.int32)
+    ke[::2] |= 1                                   # odd ends on even rows
+    ke[1::2] &= ~1                                 # even ends on odd rows
+    ke = np.minimum(ke, skv - 1).astype(np.int32)
+    for r in range(sq):
+        x[r, ke[r]] = 1.0e30                       # just past the range
+        x[r, ke[r] - 1] = 5.0e29                   # the range's last column
+    log(f"[topk] range ends bound the reads Skv={skv}")
+    for bf16 in (False, True):
+        xs, t = x, dev(x)
+        if bf16:
+            bits = synth.encode_bf16(x)
+            xs = synth.decode_bf16(bits).reshape(x.shape)
+            t = dev(bits.view(np.int16)).view(torch.bfloat16)
+        got = mq.mqa_logits_topk(t, 2048, dev(ks), dev(ke)).cpu().numpy()
+        want = oracle.topk_indices(xs, 2048, ks, ke)
+        assert np.array_equal(got, want), f"bf16={bf16}"
+        for r in range(sq):
+            assert ke[r] - 1 in got[r] and ke[r] not in got[r], f"row {r} bf16={bf16}"
