@@ -945,19 +945,23 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_reg_kernel(TopkParams p)
   ordered_write<kWords>(gmap, qmap, need_eq, p.topk, s, out, sh);
 }
 
-// Rows of 32769 .. 65536 columns: the register kernel's prefilter with the
-// row loaded in two halves of 32 keys per thread (each counted and listed in
-// turn), so the block stays within 64 VGPRs and two blocks share a compute
-// unit; the sample is loaded apart, before the row.  A row the prefilter
-// does not settle (at most topk candidates, topk above half the list, too
-// few keys >= T, a full list) is read again by the streaming selection.
-template <int IN>
-__global__ __launch_bounds__(kTopkThreads, 8) void topk_half_kernel(TopkParams p) {
-  constexpr int kTiles = 16, kHalf = 8;
+// Rows of up to kParts * 32768 columns (kParts = 2: 32769 .. 65536; 4: up to
+// 131072): the register kernel's prefilter with the row loaded in kParts
+// parts of 32 keys per thread (each counted and listed in turn), so the block
+// stays within 64 VGPRs and about 73 KB of LDS and two blocks share a compute
+// unit; the sample (4 keys per thread and 32768 columns) is loaded apart,
+// before the row.  A row the prefilter does not settle (at most topk
+// candidates, topk above half the list, too few keys >= T, a full list) is
+// read again by the streaming selection.
+template <int IN, int kParts>
+__global__ __launch_bounds__(kTopkThreads, 8) void topk_parts_kernel(TopkParams p) {
+  static_assert(kParts == 2 || kParts == 4, "two or four parts");
+  constexpr int kHalf = 8;                     // tiles per part
+  constexpr int kTiles = kParts * kHalf;
   constexpr int kTile = 4 * kTopkThreads;
   constexpr int kWords = kTiles * kTile / 32;
-  constexpr int kCap = 6144;
-  constexpr int kSamples = 4;
+  constexpr int kCap = kParts == 2 ? 6144 : 4096;
+  constexpr int kSamples = 2 * kParts;
   __shared__ TopkShared sh;
   __shared__ union {
     struct {
@@ -1004,7 +1008,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_half_kernel(TopkParams p
   const bool t_ok = T > kKeyNegInf;
   int32_t lmax = INT32_MIN;
 #pragma nounroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kParts; ++h) {
     uint32_t k[kHalf][4];
 #pragma unroll
     for (int m = 0; m < kHalf; ++m) {
@@ -1038,7 +1042,9 @@ static hipError_t launch_topk_in(const TopkParams& p, hipStream_t s) {
   } else if (p.skv <= 32 * kTopkThreads) {
     hipLaunchKernelGGL((topk_reg_kernel<IN, 32>), grid, block, 0, s, p);
   } else if (p.skv <= 64 * kTopkThreads) {
-    hipLaunchKernelGGL((topk_half_kernel<IN>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((topk_parts_kernel<IN, 2>), grid, block, 0, s, p);
+  } else if (p.skv <= 128 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_parts_kernel<IN, 4>), grid, block, 0, s, p);
   } else {
     hipLaunchKernelGGL((topk_stream_kernel<IN>), grid, block, 0, s, p);
   }

@@ -174,12 +174,12 @@ def _prefilter_rows(skv, rng):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("skv", [6000, 12000, 32768, 65536])
+@pytest.mark.parametrize("skv", [6000, 12000, 32768, 65536, 100000, 131072])
 @pytest.mark.parametrize("topk", [1, 2048, 2560, 2561, 4096])
 def test_topk_prefilter_outcomes(skv, topk):
     # every outcome must give the oracle's selection bit for bit, whichever
     # path the kernel took (topk 2560 is the largest the 32-key kernels
-    # prefilter, 4096 the 64-key kernel's)
+    # prefilter, 3072 and 2048 those of rows in two and four parts)
     import mqa_logits_amd as mq
     rng = np.random.default_rng(skv + topk)
     x = _prefilter_rows(skv, rng)
