@@ -312,3 +312,19 @@ def test_topk_range_ends_bound_the_reads(skv):
         assert np.array_equal(got, want), f"bf16={bf16}"
         for r in range(sq):
             assert ke[r] - 1 in got[r] and ke[r] not in got[r], f"row {r} bf16={bf16}"
+
+
+@pytest.mark.parametrize("skv", [5000, 40000, 100000, 140000])
+def test_topk_indices_into_a_wider_buffer(skv):
+    # the indices' row stride is passed apart: rows of topk inside a wider
+    # int32 buffer, whose guard columns every kernel (register, two and four
+    # parts, streaming) leaves alone
+    import mqa_logits_amd as mq
+    sq, topk, width = 6, 2048, 2048 + 37
+    x, ks, ke = synth.topk_logits(sq, skv, skv + 3, ties=True, ranges=True)
+    buf = torch.full((sq, width), -777, dtype=torch.int32, device="cuda")
+    log(f"[topk] indices into a wider buffer Skv={skv}")
+    mq.mqa_logits_topk(dev(x), topk, dev(ks), dev(ke), out=buf[:, :topk])
+    got = buf.cpu().numpy()
+    assert np.all(got[:, topk:] == -777), "guard columns written"
+    assert np.array_equal(got[:, :topk], oracle.topk_indices(x, topk, ks, ke))
