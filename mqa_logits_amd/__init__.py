@@ -114,26 +114,31 @@ class _Args:
     def want(self, t, name, shape, dtypes=None, itemsize=None, rows=False):
         if t is None:
             raise ValueError(f"{name} is required")
-        if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
-            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-        if dtypes is not None and t.dtype not in dtypes:
-            raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
-        if itemsize is not None and t.element_size() != itemsize:
-            raise ValueError(f"{name} must have {itemsize}-byte elements, got {t.dtype}")
+        got = t.shape                           # a tuple: compared whole when no entry is free
+        if (got != shape) if None not in shape else (
+                len(got) != len(shape) or not all(w is None or g == w for g, w in zip(got, shape))):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(got)}")
+        dt = t.dtype
+        if dtypes is not None and dt not in dtypes:
+            raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, got {dt}")
+        if itemsize is not None and dt.itemsize != itemsize:
+            raise ValueError(f"{name} must have {itemsize}-byte elements, got {dt}")
         if rows:
-            if t.stride(-1) != 1:
+            if len(got) and t.stride(-1) != 1 and got[-1] > 1:
                 raise ValueError(f"{name} rows must be contiguous")
         elif not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         self.seen.append((name, t))
 
     def on_gpu(self):
-        first = self.seen[0][1].device
+        # device indices compared as integers (-1 for a CPU tensor)
+        first = self.seen[0][1].get_device()
         for name, t in self.seen:
-            if not t.is_cuda:
+            dev = t.get_device()
+            if dev < 0:
                 raise ValueError(f"{name} must be a GPU tensor (the library reads device memory)")
-            if t.device != first:
-                raise ValueError(f"{name} must be on {first}, got {t.device}")
+            if dev != first:
+                raise ValueError(f"{name} must be on cuda:{first}, got {t.device}")
 
 
 def _codes(a, fmt, q, kv, q_sf, kv_sf, kv_scale, rows_shape, kv_shape):
